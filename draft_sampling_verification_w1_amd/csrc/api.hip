@@ -1,0 +1,355 @@
+// api.hip -- the C ABI (include/dspark.h): host-side validation, workspace
+// carving and the launch sequence of each stage.  Host code only.
+#include <stdarg.h>
+#include <stdio.h>
+
+#include <string>
+
+#include "dspark.h"
+#include "kernels.h"
+
+using namespace dspark;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+int ok() {
+  g_last_error.clear();
+  return DSPARK_OK;
+}
+
+int hip_fail(hipError_t e, const char* where) {
+  return fail(DSPARK_ERR_HIP, "%s: %s", where, hipGetErrorString(e));
+}
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t x) { return (x + kAlign - 1) & ~(kAlign - 1); }
+
+int check_problem(const dspark_problem* p) {
+  if (!p) return fail(DSPARK_ERR_ARG, "problem is NULL");
+  if (p->dtype != DSPARK_F32 && p->dtype != DSPARK_BF16)
+    return fail(DSPARK_ERR_DTYPE, "dtype %d is not DSPARK_F32 or DSPARK_BF16", p->dtype);
+  if (p->reserved != 0) return fail(DSPARK_ERR_ARG, "reserved field must be 0");
+  if (p->R < 1 || p->R > 65536) return fail(DSPARK_ERR_SHAPE, "R=%d outside [1, 65536]", p->R);
+  if (p->gamma < 1 || p->gamma > 64)
+    return fail(DSPARK_ERR_SHAPE, "gamma=%d outside [1, 64]", p->gamma);
+  if (p->V < 1 || p->V >= (1 << 26)) return fail(DSPARK_ERR_SHAPE, "V=%d outside [1, 2^26)", p->V);
+  if (p->rank != kRank) return fail(DSPARK_ERR_SHAPE, "rank=%d, only %d is supported", p->rank, kRank);
+  if ((int64_t)p->R * p->gamma > (1 << 20))
+    return fail(DSPARK_ERR_SHAPE, "R*gamma=%lld exceeds 2^20", (long long)p->R * p->gamma);
+  return DSPARK_OK;
+}
+
+// Workspace layout.  Draft and verify run one after the other on a stream,
+// so they share one buffer (the size is the larger of the two layouts).
+struct Carver {
+  size_t off = 0;
+  size_t take(size_t bytes) {
+    const size_t o = off;
+    off = align_up(off + bytes);
+    return o;
+  }
+};
+
+struct DraftLayout {
+  BiasGeometry g;
+  size_t pm, ps, cs, ci, ca, bytes;
+};
+
+DraftLayout draft_layout(const dspark_problem* p) {
+  DraftLayout L;
+  L.g = bias_geometry(p->R, p->V);
+  const size_t n = (size_t)p->R * L.g.nsplit;
+  Carver c;
+  L.pm = c.take(n * sizeof(float));
+  L.ps = c.take(n * sizeof(double));
+  L.cs = c.take(n * sizeof(double));
+  L.ci = c.take(n * sizeof(int32_t));
+  L.ca = c.take(n * sizeof(double));
+  L.bytes = c.off;
+  return L;
+}
+
+struct VerifyLayout {
+  BiasGeometry gc, gr;
+  int ns_t, chunk_t, ns_b, chunk_b;
+  size_t row_ids, counts, req_off, req_len, req_slot, req_mode, resid_ids, bonus_ids;
+  size_t lt_m, lt_s, lse_t, c_s, r_score, r_idx, r_fscore, r_fidx, b_score, b_idx, bytes;
+};
+
+VerifyLayout verify_layout(const dspark_problem* p) {
+  VerifyLayout L;
+  const size_t R = p->R, rows = (size_t)p->R * p->gamma;
+  L.gc = bias_geometry((int)rows, p->V);
+  L.gr = bias_geometry(p->R, p->V);
+  L.ns_t = row_split_count((int)rows, p->V, &L.chunk_t);
+  L.ns_b = row_split_count(p->R, p->V, &L.chunk_b);
+  Carver c;
+  L.row_ids = c.take(rows * 4);
+  L.counts = c.take(4 * 4);
+  L.req_off = c.take(R * 4);
+  L.req_len = c.take(R * 4);
+  L.req_slot = c.take(R * 4);
+  L.req_mode = c.take(R * 4);
+  L.resid_ids = c.take(R * 4);
+  L.bonus_ids = c.take(R * 4);
+  L.lt_m = c.take(rows * L.ns_t * sizeof(float));
+  L.lt_s = c.take(rows * L.ns_t * sizeof(double));
+  L.lse_t = c.take(R * (p->gamma + 1) * sizeof(double));
+  L.c_s = c.take(rows * L.gc.nsplit * sizeof(double));
+  L.r_score = c.take(R * L.gr.nsplit * sizeof(double));
+  L.r_idx = c.take(R * L.gr.nsplit * sizeof(int32_t));
+  L.r_fscore = c.take(R * L.gr.nsplit * sizeof(double));
+  L.r_fidx = c.take(R * L.gr.nsplit * sizeof(int32_t));
+  L.b_score = c.take(R * L.ns_b * sizeof(double));
+  L.b_idx = c.take(R * L.ns_b * sizeof(int32_t));
+  L.bytes = c.off;
+  return L;
+}
+
+size_t workspace_bytes(const dspark_problem* p) {
+  const size_t a = draft_layout(p).bytes, b = verify_layout(p).bytes;
+  return a > b ? a : b;
+}
+
+int check_ws(const dspark_problem* p, void* ws, size_t ws_bytes) {
+  const size_t need = workspace_bytes(p);
+  if (!ws) return fail(DSPARK_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", need);
+  if ((uintptr_t)ws % kAlign) return fail(DSPARK_ERR_WORKSPACE, "workspace not %zu-byte aligned", kAlign);
+  if (ws_bytes < need)
+    return fail(DSPARK_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", ws_bytes, need);
+  return DSPARK_OK;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Vector loads of U / T rows need 16-byte aligned rows: aligned bases and a
+// row length that keeps every row start aligned.
+int rows_vec_ok(const dspark_problem* p, const void* U, const void* T) {
+  const int per = p->dtype == DSPARK_BF16 ? 8 : 4;
+  return (p->V % per == 0) && (!U || aligned16(U)) && (!T || aligned16(T));
+}
+
+int check_weights(const void* W1, const void* W2p) {
+  if (!aligned16(W1)) return fail(DSPARK_ERR_ARG, "W1 must be 16-byte aligned");
+  if (!aligned16(W2p)) return fail(DSPARK_ERR_ARG, "W2p must be 16-byte aligned");
+  return DSPARK_OK;
+}
+
+template <typename T>
+T* at(void* base, size_t off) {
+  return reinterpret_cast<T*>(static_cast<char*>(base) + off);
+}
+
+size_t packed_bytes(const dspark_problem* p) {
+  const size_t ntiles = ((size_t)p->V + kTile - 1) / kTile;
+  return p->dtype == DSPARK_BF16 ? ntiles * kSteps * 64 * 16 : ntiles * kTile * kRank * 4;
+}
+
+}  // namespace
+
+extern "C" {
+
+__attribute__((visibility("default"))) const char* dspark_last_error(void) {
+  return g_last_error.c_str();
+}
+
+__attribute__((visibility("default"))) size_t dspark_w2_packed_bytes(const dspark_problem* p) {
+  if (check_problem(p) != DSPARK_OK) return 0;
+  return packed_bytes(p);
+}
+
+__attribute__((visibility("default"))) int dspark_pack_w2(const dspark_problem* p, const void* W2,
+                                                          void* W2p, void* stream) {
+  if (int e = check_problem(p)) return e;
+  if (!W2 || !W2p) return fail(DSPARK_ERR_ARG, "W2 and W2p must be non-NULL");
+  if ((uintptr_t)W2p % kAlign) return fail(DSPARK_ERR_ARG, "W2p must be %zu-byte aligned", kAlign);
+  hipError_t e = launch_pack_w2(p->dtype == DSPARK_BF16, p->V, W2, W2p, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "pack_w2");
+  return ok();
+}
+
+__attribute__((visibility("default"))) size_t dspark_workspace_bytes(const dspark_problem* p) {
+  if (check_problem(p) != DSPARK_OK) return 0;
+  return workspace_bytes(p);
+}
+
+__attribute__((visibility("default"))) int dspark_draft_step(
+    const dspark_problem* p, const void* U, const void* W1, const void* W2p,
+    const int32_t* anchors, int32_t* tokens, double* lse, double* logq, void* ws,
+    size_t ws_bytes, void* stream) {
+  if (int e = check_problem(p)) return e;
+  if (!U || !W1 || !W2p || !anchors || !tokens || !lse || !logq)
+    return fail(DSPARK_ERR_ARG, "draft_step: tensor pointers must be non-NULL");
+  if (int e = check_weights(W1, W2p)) return e;
+  if (int e = check_ws(p, ws, ws_bytes)) return e;
+  const bool bf16 = p->dtype == DSPARK_BF16;
+  const DraftLayout L = draft_layout(p);
+  hipStream_t s = (hipStream_t)stream;
+  BiasPassArgs a = {};
+  a.R = p->R;
+  a.gamma = p->gamma;
+  a.V = p->V;
+  a.seed = p->seed;
+  a.nrows = p->R;
+  a.U = U;
+  a.W1 = W1;
+  a.W2p = W2p;
+  a.anchors = anchors;
+  a.tokens = tokens;
+  a.ntiles = (p->V + kTile - 1) / kTile;
+  a.vec_ok = rows_vec_ok(p, U, nullptr);
+  a.tiles_per_split = L.g.tiles_per_split;
+  a.nsplit = L.g.nsplit;
+  a.pm = at<float>(ws, L.pm);
+  a.ps = at<double>(ws, L.ps);
+  a.cscore = at<double>(ws, L.cs);
+  a.cidx = at<int32_t>(ws, L.ci);
+  a.caux = at<double>(ws, L.ca);
+  for (int k = 1; k <= p->gamma; ++k) {
+    a.k = k;
+    hipError_t e = launch_bias_pass(kModeDraft, bf16, a, s);
+    if (e != hipSuccess) return hip_fail(e, "draft pass");
+    e = launch_draft_merge(p->R, p->gamma, k, a.nsplit, a.pm, a.ps, a.cscore, a.cidx, a.caux,
+                           tokens, lse, logq, s);
+    if (e != hipSuccess) return hip_fail(e, "draft merge");
+  }
+  return ok();
+}
+
+__attribute__((visibility("default"))) int dspark_verify(
+    const dspark_problem* p, const void* U, const void* W1, const void* W2p,
+    const int32_t* anchors, const int32_t* tokens, const double* lse_d, const double* logq,
+    const void* T, const int32_t* lengths, float* cstar, int32_t* n_accept, int32_t* out_token,
+    uint8_t* accept_mask, double* lse_t, void* ws, size_t ws_bytes, void* stream) {
+  if (int e = check_problem(p)) return e;
+  if (!U || !W1 || !W2p || !anchors || !tokens || !lse_d || !logq || !T || !cstar || !n_accept ||
+      !out_token)
+    return fail(DSPARK_ERR_ARG, "verify: tensor pointers must be non-NULL");
+  if (int e = check_weights(W1, W2p)) return e;
+  if (int e = check_ws(p, ws, ws_bytes)) return e;
+  const bool bf16 = p->dtype == DSPARK_BF16;
+  const VerifyLayout L = verify_layout(p);
+  hipStream_t s = (hipStream_t)stream;
+  VerifyWs w;
+  w.row_ids = at<int32_t>(ws, L.row_ids);
+  w.counts = at<int32_t>(ws, L.counts);
+  w.req_off = at<int32_t>(ws, L.req_off);
+  w.req_len = at<int32_t>(ws, L.req_len);
+  w.req_slot = at<int32_t>(ws, L.req_slot);
+  w.req_mode = at<int32_t>(ws, L.req_mode);
+  w.resid_ids = at<int32_t>(ws, L.resid_ids);
+  w.bonus_ids = at<int32_t>(ws, L.bonus_ids);
+  w.lt_m = at<float>(ws, L.lt_m);
+  w.lt_s = at<double>(ws, L.lt_s);
+  w.lse_t = at<double>(ws, L.lse_t);
+  w.c_s = at<double>(ws, L.c_s);
+  w.r_score = at<double>(ws, L.r_score);
+  w.r_idx = at<int32_t>(ws, L.r_idx);
+  w.r_fscore = at<double>(ws, L.r_fscore);
+  w.r_fidx = at<int32_t>(ws, L.r_fidx);
+  w.b_score = at<double>(ws, L.b_score);
+  w.b_idx = at<int32_t>(ws, L.b_idx);
+  w.ns_t = L.ns_t;
+  w.ns_c = L.gc.nsplit;
+  w.ns_r = L.gr.nsplit;
+  w.ns_b = L.ns_b;
+  w.tps_t = L.chunk_t;
+  w.tps_b = L.chunk_b;
+  w.vec_ok = rows_vec_ok(p, nullptr, T);
+
+  hipError_t e = launch_build_rows(p->R, p->gamma, lengths, w, s);
+  if (e != hipSuccess) return hip_fail(e, "verify rows");
+  e = launch_target_lse(bf16, p->R, p->gamma, p->V, T, w, s);
+  if (e != hipSuccess) return hip_fail(e, "target lse");
+  e = launch_decide(bf16, p->R, p->gamma, p->V, p->seed, T, tokens, logq, w, n_accept, accept_mask,
+                    lse_t, s);
+  if (e != hipSuccess) return hip_fail(e, "decide");
+
+  BiasPassArgs a = {};
+  a.R = p->R;
+  a.gamma = p->gamma;
+  a.V = p->V;
+  a.seed = p->seed;
+  a.U = U;
+  a.T = T;
+  a.W1 = W1;
+  a.W2p = W2p;
+  a.anchors = anchors;
+  a.tokens = tokens;
+  a.lse_d = lse_d;
+  a.lse_t = w.lse_t;
+  a.ntiles = (p->V + kTile - 1) / kTile;
+  a.vec_ok = rows_vec_ok(p, U, T);
+  // c* over every verified row
+  a.row_ids = w.row_ids;
+  a.row_count = w.counts + 0;
+  a.nrows = p->R * p->gamma;
+  a.tiles_per_split = L.gc.tiles_per_split;
+  a.nsplit = L.gc.nsplit;
+  a.ps = w.c_s;
+  e = launch_bias_pass(kModeCstar, bf16, a, s);
+  if (e != hipSuccess) return hip_fail(e, "cstar pass");
+  // residual draw at each request's first rejection
+  a.row_ids = w.resid_ids;
+  a.row_count = w.counts + 1;
+  a.nrows = p->R;
+  a.tiles_per_split = L.gr.tiles_per_split;
+  a.nsplit = L.gr.nsplit;
+  a.ps = nullptr;
+  a.cscore = w.r_score;
+  a.cidx = w.r_idx;
+  a.fscore = w.r_fscore;
+  a.fidx = w.r_fidx;
+  e = launch_bias_pass(kModeResidual, bf16, a, s);
+  if (e != hipSuccess) return hip_fail(e, "residual pass");
+  e = launch_bonus(bf16, p->R, p->gamma, p->V, p->seed, T, w, s);
+  if (e != hipSuccess) return hip_fail(e, "bonus pass");
+  e = launch_finalize(p->R, p->gamma, w, cstar, out_token, s);
+  if (e != hipSuccess) return hip_fail(e, "finalize");
+  return ok();
+}
+
+__attribute__((visibility("default"))) int dspark_confidence(
+    const dspark_problem* p, int32_t H, const uint16_t* h, const float* w, const float* temps,
+    const void* W1, const int32_t* anchors, const int32_t* tokens, float* c, void* stream) {
+  if (int e = check_problem(p)) return e;
+  if (H < 1 || H > 65536) return fail(DSPARK_ERR_SHAPE, "H=%d outside [1, 65536]", H);
+  if (!h || !w || !temps || !W1 || !anchors || !tokens || !c)
+    return fail(DSPARK_ERR_ARG, "confidence: tensor pointers must be non-NULL");
+  hipError_t e = launch_confidence(p->dtype == DSPARK_BF16, p->R, p->gamma, p->V, H, h, w, temps,
+                                   W1, anchors, tokens, c, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "confidence");
+  return ok();
+}
+
+__attribute__((visibility("default"))) int dspark_schedule(int32_t R, int32_t gamma,
+                                                           const float* c, const float* sps,
+                                                           int32_t n_sps, float* a,
+                                                           int32_t* lengths, double* stats,
+                                                           double* theta_path, void* stream) {
+  if (R < 1 || gamma < 1) return fail(DSPARK_ERR_SHAPE, "R=%d, gamma=%d must be >= 1", R, gamma);
+  if ((int64_t)R * gamma > 16384)
+    return fail(DSPARK_ERR_SHAPE, "R*gamma=%lld exceeds 16384", (long long)R * gamma);
+  if ((int64_t)n_sps < (int64_t)R * (gamma + 1))
+    return fail(DSPARK_ERR_RANGE, "SPS table has %d entries, R*(gamma+1)=%lld needed", n_sps,
+                (long long)R * (gamma + 1));
+  if (!c || !sps || !a || !lengths || !stats)
+    return fail(DSPARK_ERR_ARG, "schedule: tensor pointers must be non-NULL");
+  hipError_t e = launch_schedule(R, gamma, c, sps, a, lengths, stats, theta_path, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "schedule");
+  return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,199 @@
+// device_common.h -- gfx950 device primitives for the DSpark hot path:
+// counter-based noise, bf16 unpacking, wave64 exchanges and the partial-result
+// records the split-vocabulary kernels hand to their merge kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "kernels.h"
+
+namespace dspark {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// Random-number streams (one per kind of draw).
+constexpr uint32_t kStreamDraft = 0, kStreamAccept = 1, kStreamResidual = 2, kStreamBonus = 3;
+
+// ---------------------------------------------------------------------------
+// Philox4x32-10 (Salmon, Moraes, Dror, Shaw, SC'11): ten rounds of two
+// 32x32->64 multiplies, a word permutation and a key xor; the key advances by
+// the Weyl increments between rounds.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ u32x4 philox4x32_10(u32x4 x, uint32_t k0, uint32_t k1) {
+#pragma unroll
+  for (int round = 0; round < 10; ++round) {
+    const uint64_t lo_hi0 = (uint64_t)0xD2511F53u * (uint64_t)x.x;
+    const uint64_t lo_hi1 = (uint64_t)0xCD9E8D57u * (uint64_t)x.z;
+    u32x4 y;
+    y.x = (uint32_t)(lo_hi1 >> 32) ^ x.y ^ k0;
+    y.y = (uint32_t)lo_hi1;
+    y.z = (uint32_t)(lo_hi0 >> 32) ^ x.w ^ k1;
+    y.w = (uint32_t)lo_hi0;
+    x = y;
+    k0 += 0x9E3779B9u;
+    k1 += 0xBB67AE85u;
+  }
+  return x;
+}
+
+// Four words for vocabulary entries 4g .. 4g+3 of row (stream, r, k).
+__device__ __forceinline__ u32x4 noise_block(uint64_t seed, uint32_t stream, uint32_t r,
+                                             uint32_t k, uint32_t group) {
+  u32x4 c;
+  c.x = group;
+  c.y = k;
+  c.z = r;
+  c.w = stream;
+  return philox4x32_10(c, (uint32_t)seed, (uint32_t)(seed >> 32));
+}
+
+__device__ __forceinline__ uint32_t word_of(u32x4 b, int i) {
+  return i == 0 ? b.x : (i == 1 ? b.y : (i == 2 ? b.z : b.w));
+}
+
+// Uniform ((w>>9) + 1/2) 2^-23, exact in binary32.
+__device__ __forceinline__ float uniform_f32(uint32_t w) {
+  return fmaf((float)(w >> 9), 0x1p-23f, 0x1p-24f);
+}
+
+__device__ __forceinline__ double uniform_f64(uint32_t w) {
+  return ((double)(w >> 9) + 0.5) * 0x1p-23;
+}
+
+// -ln(u) in binary32 with small relative error everywhere: a short series in
+// a = 1 - u (exact here) when u is within 2^-6 of 1, the hardware log2 otherwise.
+__device__ __forceinline__ float neg_log_uniform_f32(uint32_t w) {
+  const float u = uniform_f32(w);
+  const float a = 1.0f - u;
+  const float series =
+      a * fmaf(a, fmaf(a, fmaf(a, fmaf(a, 0.2f, 0.25f), 0.33333334f), 0.5f), 1.0f);
+  const float via_log = -__builtin_amdgcn_logf(u) * kLn2;
+  return a < 0x1p-6f ? series : via_log;
+}
+
+// Gumbel variate for screening candidates (binary32).
+__device__ __forceinline__ float gumbel_f32(uint32_t w) {
+  return -__builtin_amdgcn_logf(neg_log_uniform_f32(w)) * kLn2;
+}
+
+// Gumbel variate for final decisions (binary64).
+__device__ __forceinline__ double gumbel_f64(uint32_t w) {
+  return -log(-log(uniform_f64(w)));
+}
+
+__device__ __forceinline__ float exp_fast(float x) {  // e^x via the hardware exp2
+  return __builtin_amdgcn_exp2f(x * kLog2e);
+}
+
+// ---------------------------------------------------------------------------
+// bf16 / f32 element access
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float bf16_lo(uint32_t pair) { return __uint_as_float(pair << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t pair) { return __uint_as_float(pair & 0xFFFF0000u); }
+__device__ __forceinline__ float bf16_at(const uint16_t* p, int64_t i) {
+  return __uint_as_float((uint32_t)p[i] << 16);
+}
+
+// Load 16 consecutive elements [v, v+16) of a row into floats; entries at or
+// beyond V read as -inf.  `vec_ok` (row base 16-byte aligned) enables vector loads.
+__device__ __forceinline__ void load16(const uint16_t* row, int v, int V, bool vec_ok, float* out) {
+  if (vec_ok && v + 16 <= V) {
+    const u32x4* p = reinterpret_cast<const u32x4*>(row + v);
+    const u32x4 a = __builtin_nontemporal_load(p);
+    const u32x4 b = __builtin_nontemporal_load(p + 1);
+    const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      out[2 * i] = bf16_lo(w[i]);
+      out[2 * i + 1] = bf16_hi(w[i]);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) out[i] = (v + i < V) ? bf16_at(row, v + i) : -INFINITY;
+  }
+}
+
+__device__ __forceinline__ void load16(const float* row, int v, int V, bool vec_ok, float* out) {
+  if (vec_ok && v + 16 <= V) {
+    const f32x4* p = reinterpret_cast<const f32x4*>(row + v);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const f32x4 q = __builtin_nontemporal_load(p + i);
+      out[4 * i] = q.x;
+      out[4 * i + 1] = q.y;
+      out[4 * i + 2] = q.z;
+      out[4 * i + 3] = q.w;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) out[i] = (v + i < V) ? row[v + i] : -INFINITY;
+  }
+}
+
+__device__ __forceinline__ float elem_at(const uint16_t* p, int64_t i) { return bf16_at(p, i); }
+__device__ __forceinline__ float elem_at(const float* p, int64_t i) { return p[i]; }
+
+// ---------------------------------------------------------------------------
+// Online log-sum-exp state and Gumbel-argmax candidates.
+// ---------------------------------------------------------------------------
+struct LseState {
+  float m;   // running maximum (binary32 values seen)
+  double s;  // sum of exp(x - m)
+};
+
+__device__ __forceinline__ void lse_init(LseState& st) {
+  st.m = -INFINITY;
+  st.s = 0.0;
+}
+
+// Merge two (m, s) pairs in binary64.
+__device__ __forceinline__ void lse_merge(float& m, double& s, float m2, double s2) {
+  if (m2 == -INFINITY) return;
+  if (m == -INFINITY) {
+    m = m2;
+    s = s2;
+    return;
+  }
+  if (m2 > m) {
+    s = s * exp((double)m - (double)m2) + s2;
+    m = m2;
+  } else {
+    s = s + s2 * exp((double)m2 - (double)m);
+  }
+}
+
+// Candidate order: larger score wins; equal scores -> lower index.
+__device__ __forceinline__ bool cand_better(double s1, int i1, double s2, int i2) {
+  return (s1 > s2) || (s1 == s2 && (unsigned)i1 < (unsigned)i2);
+}
+
+// Lane exchange across the two halves of a wave64.
+template <typename T>
+__device__ __forceinline__ T xor32(T v) {
+  return __shfl_xor(v, 32, 64);
+}
+
+// ---------------------------------------------------------------------------
+// Partial records written per (vocabulary split, row) and merged later.
+// Arrays are structure-of-arrays with row stride `ld` (the row capacity).
+// ---------------------------------------------------------------------------
+struct LsePartials {
+  float* m;
+  double* s;
+};
+
+struct CandPartials {
+  double* score;  // refined binary64 score, -inf if none
+  int32_t* idx;   // token id, -1 if none
+  double* aux;    // mode dependent: draft z at the candidate
+};
+
+}  // namespace dspark

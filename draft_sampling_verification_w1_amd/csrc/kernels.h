@@ -1,0 +1,113 @@
+// kernels.h -- host-side launchers shared between the kernel translation units
+// and the C-ABI layer.  Every launcher only enqueues work on `stream`.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dspark {
+
+constexpr int kRank = 256;       // Markov-head rank (summary page §3.1 default)
+constexpr int kTile = 32;        // vocabulary entries per MFMA tile
+constexpr int kSteps = kRank / 16;
+
+enum BiasMode { kModeDraft = 0, kModeCstar = 1, kModeResidual = 2 };
+
+// Arguments of one split-vocabulary pass over a set of (request, position)
+// rows: bias B = W1[x_{k-1}] W2 plus backbone logits U, consumed by a
+// mode-specific epilogue.  Partial records are indexed [row * nsplit + split].
+struct BiasPassArgs {
+  int R, gamma, V;
+  uint64_t seed;
+  int k;                      // draft: 1-based block position of every row
+  const int32_t* row_ids;     // verify passes: row id r*gamma + (k-1); null in draft
+  const int32_t* row_count;   // verify passes: device count of valid rows
+  int nrows;                  // row capacity
+  const void* U;
+  const void* T;
+  const void* W1;
+  const void* W2p;
+  const int32_t* anchors;
+  const int32_t* tokens;
+  const double* lse_d;        // [R*gamma]
+  const double* lse_t;        // [R*(gamma+1)]
+  int ntiles;                 // ceil(V / 32)
+  int vec_ok;                 // U/T rows 16-byte aligned: vector loads allowed
+  int tiles_per_split;
+  int nsplit;
+  float* pm;                  // draft: running max per partial
+  double* ps;                 // draft: sum of exp; cstar: sum of min(p^d, p^t)
+  double* cscore;             // candidate partials (draft, residual)
+  int32_t* cidx;
+  double* caux;               // draft: z at the candidate
+  double* fscore;             // residual pass: fallback candidates over ln p^t
+  int32_t* fidx;
+};
+
+struct BiasGeometry {
+  int rows_per_block;  // 256
+  int row_blocks;
+  int tiles_per_split;
+  int nsplit;
+};
+BiasGeometry bias_geometry(int nrows, int V);
+
+hipError_t launch_bias_pass(int mode, bool bf16, const BiasPassArgs& a, hipStream_t stream);
+
+// Merge draft partials of position k into tokens / lse / logq.
+hipError_t launch_draft_merge(int R, int gamma, int k, int nsplit, const float* pm,
+                              const double* ps, const double* cscore, const int32_t* cidx,
+                              const double* caux, int32_t* tokens, double* lse, double* logq,
+                              hipStream_t stream);
+
+// ---- verification helpers ------------------------------------------------
+struct VerifyWs {
+  int32_t* row_ids;     // [R*gamma]
+  int32_t* counts;      // [4]: rows, residual rows, bonus rows, spare
+  int32_t* req_off;     // [R] first row of request r in row_ids
+  int32_t* req_len;     // [R] clamped verify length
+  int32_t* req_slot;    // [R] slot of r in the residual or bonus list
+  int32_t* req_mode;    // [R] 1 residual, 2 bonus
+  int32_t* resid_ids;   // [R] row ids r*gamma + (k*-1)
+  int32_t* bonus_ids;   // [R] target row ids r*(gamma+1) + l_r
+  float* lt_m;          // [R*gamma*ns_t] target log-sum-exp partials
+  double* lt_s;
+  double* lse_t;        // [R*(gamma+1)] merged, NaN where not computed
+  double* c_s;          // [R*gamma*ns_c] c* partial sums
+  double* r_score;      // [R*ns_r] residual candidates
+  int32_t* r_idx;
+  double* r_fscore;
+  int32_t* r_fidx;
+  double* b_score;      // [R*ns_b] bonus candidates
+  int32_t* b_idx;
+  int ns_t, ns_c, ns_r, ns_b;
+  int tps_t, tps_b;     // elements per split for the row-streaming passes
+  int vec_ok;           // T rows 16-byte aligned: vector loads allowed
+};
+
+int row_split_count(int rows, int V, int* chunk);
+
+hipError_t launch_build_rows(int R, int gamma, const int32_t* lengths, const VerifyWs& w,
+                             hipStream_t stream);
+hipError_t launch_target_lse(bool bf16, int R, int gamma, int V, const void* T,
+                             const VerifyWs& w, hipStream_t stream);
+hipError_t launch_decide(bool bf16, int R, int gamma, int V, uint64_t seed, const void* T,
+                         const int32_t* tokens, const double* logq, const VerifyWs& w,
+                         int32_t* n_accept, uint8_t* accept_mask, double* lse_t_out,
+                         hipStream_t stream);
+hipError_t launch_bonus(bool bf16, int R, int gamma, int V, uint64_t seed, const void* T,
+                        const VerifyWs& w, hipStream_t stream);
+hipError_t launch_finalize(int R, int gamma, const VerifyWs& w, float* cstar,
+                           int32_t* out_token, hipStream_t stream);
+
+// ---- other stages ---------------------------------------------------------
+hipError_t launch_pack_w2(bool bf16, int V, const void* W2, void* W2p, hipStream_t stream);
+hipError_t launch_confidence(bool w1_bf16, int R, int gamma, int V, int H, const uint16_t* h,
+                             const float* w, const float* temps, const void* W1,
+                             const int32_t* anchors, const int32_t* tokens, float* c,
+                             hipStream_t stream);
+hipError_t launch_schedule(int R, int gamma, const float* c, const float* sps, float* a,
+                           int32_t* lengths, double* stats, double* theta_path,
+                           hipStream_t stream);
+
+}  // namespace dspark

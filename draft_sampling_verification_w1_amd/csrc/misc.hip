@@ -1,0 +1,98 @@
+// misc.hip -- W2 packing (once per model) and the confidence head.
+#include "device_common.h"
+#include "kernels.h"
+
+namespace dspark {
+
+namespace {
+
+// Packed bf16 W2: tile t of 32 tokens, step s of 16 rank indices, lane l:
+// the 8 values W2[128*(l/32) + 8*s + e][32*t + pi(l%32)], e = 0..7, where
+// pi(m) = 16*((m>>2)&1) + 4*(m>>3) + (m&3) undoes the MFMA 32x32 output row
+// order so that each lane ends up with 16 consecutive tokens.
+__global__ __launch_bounds__(256) void k_pack_w2_bf16(int V, int ntiles, const uint16_t* W2,
+                                                      u32x4* out) {
+  const int64_t g = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (g >= (int64_t)ntiles * kSteps * 64) return;
+  const int l = (int)(g & 63);
+  const int s = (int)((g >> 6) % kSteps);
+  const int t = (int)(g / (64 * kSteps));
+  const int m = l & 31;
+  const int v = t * kTile + 16 * ((m >> 2) & 1) + 4 * (m >> 3) + (m & 3);
+  const int k0 = 128 * (l >> 5) + 8 * s;
+  uint32_t w[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const uint32_t lo = v < V ? W2[(int64_t)(k0 + 2 * e) * V + v] : 0u;
+    const uint32_t hi = v < V ? W2[(int64_t)(k0 + 2 * e + 1) * V + v] : 0u;
+    w[e] = lo | (hi << 16);
+  }
+  out[g] = (u32x4){w[0], w[1], w[2], w[3]};
+}
+
+// Transposed f32 W2: out[v][i] = W2[i][v], zero rows for v >= V.
+__global__ __launch_bounds__(256) void k_pack_w2_f32(int V, int vpad, const float* W2, float* out) {
+  const int64_t g = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (g >= (int64_t)vpad * kRank) return;
+  const int i = (int)(g % kRank);
+  const int v = (int)(g / kRank);
+  out[g] = v < V ? W2[(int64_t)i * V + v] : 0.0f;
+}
+
+// Confidence head with per-position temperature (summary page §3.2.1):
+// c = sigmoid((w . [h_k; W1[x_{k-1}]]) / T_k), one wave per row, binary64 sums.
+template <typename E>
+__global__ __launch_bounds__(256) void k_confidence(int R, int gamma, int V, int H,
+                                                    const uint16_t* h, const float* w,
+                                                    const float* temps, const E* W1,
+                                                    const int32_t* anchors, const int32_t* tokens,
+                                                    float* c) {
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= R * gamma) return;
+  const int r = row / gamma;
+  const int k = row - r * gamma + 1;
+  int x = (k == 1) ? anchors[r] : tokens[(int64_t)r * gamma + (k - 2)];
+  x = min(max(x, 0), V - 1);
+  const uint16_t* hr = h + (int64_t)row * H;
+  double s = 0.0;
+  for (int i = lane; i < H; i += 64) s += (double)w[i] * (double)bf16_at(hr, i);
+  for (int j = lane; j < kRank; j += 64)
+    s += (double)w[H + j] * (double)elem_at(W1, (int64_t)x * kRank + j);
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) s += __shfl_xor(s, off, 64);
+  if (lane == 0) c[row] = (float)(1.0 / (1.0 + exp(-s / (double)temps[k - 1])));
+}
+
+}  // namespace
+
+hipError_t launch_pack_w2(bool bf16, int V, const void* W2, void* W2p, hipStream_t stream) {
+  const int ntiles = (V + kTile - 1) / kTile;
+  if (bf16) {
+    const int64_t n = (int64_t)ntiles * kSteps * 64;
+    hipLaunchKernelGGL(k_pack_w2_bf16, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, V,
+                       ntiles, (const uint16_t*)W2, (u32x4*)W2p);
+  } else {
+    const int64_t n = (int64_t)ntiles * kTile * kRank;
+    hipLaunchKernelGGL(k_pack_w2_f32, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, V,
+                       ntiles * kTile, (const float*)W2, (float*)W2p);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_confidence(bool w1_bf16, int R, int gamma, int V, int H, const uint16_t* h,
+                             const float* w, const float* temps, const void* W1,
+                             const int32_t* anchors, const int32_t* tokens, float* c,
+                             hipStream_t stream) {
+  const int rows = R * gamma;
+  const dim3 grid((rows + 3) / 4);
+  if (w1_bf16)
+    hipLaunchKernelGGL(k_confidence<uint16_t>, grid, dim3(256), 0, stream, R, gamma, V, H, h, w,
+                       temps, (const uint16_t*)W1, anchors, tokens, c);
+  else
+    hipLaunchKernelGGL(k_confidence<float>, grid, dim3(256), 0, stream, R, gamma, V, H, h, w, temps,
+                       (const float*)W1, anchors, tokens, c);
+  return hipGetLastError();
+}
+
+}  // namespace dspark

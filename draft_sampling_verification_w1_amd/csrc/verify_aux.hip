@@ -1,0 +1,384 @@
+// verify_aux.hip -- the verification steps that need no Markov-head bias:
+//   build_rows : (request, position) rows to verify, k <= l_r
+//   target_lse : log-sum-exp of every verified target row (split vocabulary)
+//   decide     : acceptance test of each drafted token, first rejection,
+//                residual / bonus work lists (standard speculative rejection
+//                sampling; notes page 배경, summary page 요약)
+//   bonus      : Gumbel-argmax over T[r, l_r] when every verified token is
+//                accepted (bonus token from p^t_{l_r+1})
+//   finalize   : c* per row and the corrective / bonus token per request
+#include "device_common.h"
+#include "kernels.h"
+
+namespace dspark {
+
+namespace {
+
+__device__ __forceinline__ void load8(const uint16_t* row, int v, int vend, bool vec_ok, float* out) {
+  if (vec_ok && v + 8 <= vend) {
+    const u32x4 a = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(row + v));
+    out[0] = bf16_lo(a.x); out[1] = bf16_hi(a.x);
+    out[2] = bf16_lo(a.y); out[3] = bf16_hi(a.y);
+    out[4] = bf16_lo(a.z); out[5] = bf16_hi(a.z);
+    out[6] = bf16_lo(a.w); out[7] = bf16_hi(a.w);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) out[i] = (v + i < vend) ? bf16_at(row, v + i) : -INFINITY;
+  }
+}
+
+__device__ __forceinline__ void load8(const float* row, int v, int vend, bool vec_ok, float* out) {
+  if (vec_ok && v + 8 <= vend) {
+    const f32x4 a = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(row + v));
+    const f32x4 b = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(row + v) + 1);
+    out[0] = a.x; out[1] = a.y; out[2] = a.z; out[3] = a.w;
+    out[4] = b.x; out[5] = b.y; out[6] = b.z; out[7] = b.w;
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) out[i] = (v + i < vend) ? row[v + i] : -INFINITY;
+  }
+}
+
+// Block-wide (256 threads) merge of (m, s) into thread 0.
+__device__ __forceinline__ void block_lse(float& m, double& s) {
+  __shared__ float sm[4];
+  __shared__ double ss[4];
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const float m2 = __shfl_xor(m, off, 64);
+    const double s2 = __shfl_xor(s, off, 64);
+    lse_merge(m, s, m2, s2);
+  }
+  const int wave = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) {
+    sm[wave] = m;
+    ss[wave] = s;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    for (int w = 1; w < 4; ++w) lse_merge(m, s, sm[w], ss[w]);
+  }
+  __syncthreads();
+}
+
+__device__ __forceinline__ void block_best(double& sc, int& idx) {
+  __shared__ double ssc[4];
+  __shared__ int sidx[4];
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const double s2 = __shfl_xor(sc, off, 64);
+    const int i2 = __shfl_xor(idx, off, 64);
+    if (cand_better(s2, i2, sc, idx)) {
+      sc = s2;
+      idx = i2;
+    }
+  }
+  const int wave = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) {
+    ssc[wave] = sc;
+    sidx[wave] = idx;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    for (int w = 1; w < 4; ++w)
+      if (cand_better(ssc[w], sidx[w], sc, idx)) {
+        sc = ssc[w];
+        idx = sidx[w];
+      }
+  }
+  __syncthreads();
+}
+
+__global__ __launch_bounds__(1024) void k_build_rows(int R, int gamma, const int32_t* lengths,
+                                                     VerifyWs w) {
+  __shared__ int scan[1024];
+  __shared__ int carry;
+  const int tid = threadIdx.x;
+  if (tid == 0) carry = 0;
+  __syncthreads();
+  for (int base = 0; base < R; base += 1024) {
+    const int r = base + tid;
+    int L = 0;
+    if (r < R) L = lengths ? min(max(lengths[r], 0), gamma) : gamma;
+    scan[tid] = L;
+    __syncthreads();
+    for (int off = 1; off < 1024; off <<= 1) {
+      const int v = tid >= off ? scan[tid - off] : 0;
+      __syncthreads();
+      scan[tid] += v;
+      __syncthreads();
+    }
+    const int excl = carry + scan[tid] - L;
+    if (r < R) {
+      w.req_off[r] = excl;
+      w.req_len[r] = L;
+      w.req_mode[r] = 0;
+      w.req_slot[r] = 0;
+      for (int k = 1; k <= L; ++k) w.row_ids[excl + k - 1] = r * gamma + (k - 1);
+    }
+    __syncthreads();
+    if (tid == 1023) carry += scan[1023];
+    __syncthreads();
+  }
+  if (tid == 0) {
+    w.counts[0] = carry;
+    w.counts[1] = 0;
+    w.counts[2] = 0;
+    w.counts[3] = 0;
+  }
+}
+
+template <typename E>
+__global__ __launch_bounds__(256) void k_target_lse(int gamma, int V, const E* T, VerifyWs w) {
+  const int i = blockIdx.x;
+  if (i >= w.counts[0]) return;
+  const int id = w.row_ids[i];
+  const int r = id / gamma;
+  const int k = id - r * gamma + 1;
+  const E* row = T + ((int64_t)r * (gamma + 1) + (k - 1)) * (int64_t)V;
+  const int split = blockIdx.y;
+  const int v0 = split * w.tps_t;
+  const int v1 = min(V, v0 + w.tps_t);
+  const bool vec_ok = w.vec_ok != 0;
+  float m = -INFINITY;
+  double s = 0.0;
+  for (int v = v0 + 8 * threadIdx.x; v < v1; v += 8 * 256) {
+    float x[8];
+    load8(row, v, v1, vec_ok, x);
+    float mt = x[0];
+#pragma unroll
+    for (int j = 1; j < 8; ++j) mt = fmaxf(mt, x[j]);
+    if (mt > m) {
+      if (m != -INFINITY) s *= exp((double)m - (double)mt);
+      m = mt;
+    }
+    if (m != -INFINITY) {
+      float e[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) e[j] = __builtin_amdgcn_exp2f((x[j] - m) * kLog2e);
+      s += (double)(((e[0] + e[1]) + (e[2] + e[3])) + ((e[4] + e[5]) + (e[6] + e[7])));
+    }
+  }
+  block_lse(m, s);
+  if (threadIdx.x == 0) {
+    const int64_t o = (int64_t)i * w.ns_t + split;
+    w.lt_m[o] = m;
+    w.lt_s[o] = s;
+  }
+}
+
+template <typename E>
+__global__ __launch_bounds__(256) void k_decide(int R, int gamma, int V, uint64_t seed,
+                                                const E* T, const int32_t* tokens,
+                                                const double* logq, VerifyWs w,
+                                                int32_t* n_accept, uint8_t* accept_mask,
+                                                double* lse_t_out) {
+  __shared__ double lse_k[64];
+  const int r = blockIdx.x;
+  const int L = w.req_len[r];
+  const int off = w.req_off[r];
+  for (int k = 1; k <= L; ++k) {
+    const int64_t base = (int64_t)(off + k - 1) * w.ns_t;
+    float m = -INFINITY;
+    double s = 0.0;
+    for (int j = threadIdx.x; j < w.ns_t; j += 256) lse_merge(m, s, w.lt_m[base + j], w.lt_s[base + j]);
+    block_lse(m, s);
+    if (threadIdx.x == 0) lse_k[k - 1] = (double)m + log(s);
+  }
+  __syncthreads();
+  for (int k = threadIdx.x + 1; k <= gamma + 1; k += 256) {
+    const double v = (k <= L) ? lse_k[k - 1] : NAN;
+    w.lse_t[(int64_t)r * (gamma + 1) + (k - 1)] = v;
+    if (lse_t_out) lse_t_out[(int64_t)r * (gamma + 1) + (k - 1)] = v;
+  }
+  if (threadIdx.x == 0) {
+    int n = L, kstar = 0;
+    for (int k = 1; k <= gamma; ++k) {
+      uint8_t mk = 255;
+      if (k <= L && kstar == 0) {
+        const int64_t o = (int64_t)r * gamma + (k - 1);
+        const int x = min(max(tokens[o], 0), V - 1);
+        const double tx = (double)elem_at(T, ((int64_t)r * (gamma + 1) + (k - 1)) * (int64_t)V + x);
+        const double rho = (tx - lse_k[k - 1]) - logq[o];
+        const uint32_t wd = noise_block(seed, kStreamAccept, r, k, 0).x;
+        const double ln_u = log(uniform_f64(wd));
+        const bool ok = ln_u < rho;
+        mk = ok ? 1 : 0;
+        if (!ok) {
+          kstar = k;
+          n = k - 1;
+        }
+      }
+      if (accept_mask) accept_mask[(int64_t)r * gamma + (k - 1)] = mk;
+    }
+    n_accept[r] = n;
+    if (kstar > 0) {
+      const int slot = atomicAdd(&w.counts[1], 1);
+      w.resid_ids[slot] = r * gamma + (kstar - 1);
+      w.req_mode[r] = 1;
+      w.req_slot[r] = slot;
+    } else {
+      const int slot = atomicAdd(&w.counts[2], 1);
+      w.bonus_ids[slot] = r * (gamma + 1) + L;
+      w.req_mode[r] = 2;
+      w.req_slot[r] = slot;
+    }
+  }
+}
+
+template <typename E>
+__global__ __launch_bounds__(256) void k_bonus(int gamma, int V, uint64_t seed, const E* T,
+                                               VerifyWs w) {
+  const int i = blockIdx.x;
+  if (i >= w.counts[2]) return;
+  const int id = w.bonus_ids[i];
+  const int r = id / (gamma + 1);
+  const int b = id - r * (gamma + 1) + 1;
+  const E* row = T + (int64_t)id * V;
+  const int split = blockIdx.y;
+  const int v0 = split * w.tps_b;
+  const int v1 = min(V, v0 + w.tps_b);
+  const bool vec_ok = w.vec_ok != 0;
+  float best = -INFINITY, bt = 0.f;
+  int bidx = -1;
+  uint32_t bw = 0;
+  for (int v = v0 + 8 * threadIdx.x; v < v1; v += 8 * 256) {
+    float x[8];
+    load8(row, v, v1, vec_ok, x);
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const u32x4 wb = noise_block(seed, kStreamBonus, r, b, (uint32_t)(v >> 2) + q);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int j = 4 * q + e;
+        if (v + j < v1) {
+          const uint32_t wd = word_of(wb, e);
+          const float sc = x[j] + gumbel_f32(wd);
+          if (sc > best) {
+            best = sc;
+            bidx = v + j;
+            bt = x[j];
+            bw = wd;
+          }
+        }
+      }
+    }
+  }
+  double sc = bidx >= 0 ? (double)bt + gumbel_f64(bw) : -INFINITY;
+  block_best(sc, bidx);
+  if (threadIdx.x == 0) {
+    const int64_t o = (int64_t)i * w.ns_b + split;
+    w.b_score[o] = sc;
+    w.b_idx[o] = bidx;
+  }
+}
+
+__global__ __launch_bounds__(256) void k_finalize(int R, int gamma, VerifyWs w, float* cstar,
+                                                  int32_t* out_token) {
+  const int t = blockIdx.x * 256 + threadIdx.x;
+  if (t < R * gamma) {
+    const int r = t / gamma;
+    const int k = t - r * gamma + 1;
+    float c = NAN;
+    if (k <= w.req_len[r]) {
+      const int64_t base = (int64_t)(w.req_off[r] + k - 1) * w.ns_c;
+      double s = 0.0;
+      for (int j = 0; j < w.ns_c; ++j) s += w.c_s[base + j];
+      c = (float)s;
+    }
+    cstar[t] = c;
+  }
+  if (t < R) {
+    const int slot = w.req_slot[t];
+    double sc = -INFINITY;
+    int idx = -1;
+    if (w.req_mode[t] == 1) {
+      const int64_t base = (int64_t)slot * w.ns_r;
+      for (int j = 0; j < w.ns_r; ++j)
+        if (cand_better(w.r_score[base + j], w.r_idx[base + j], sc, idx)) {
+          sc = w.r_score[base + j];
+          idx = w.r_idx[base + j];
+        }
+      if (idx < 0) {  // empty residual after rounding: draw from p^t instead
+        sc = -INFINITY;
+        for (int j = 0; j < w.ns_r; ++j)
+          if (cand_better(w.r_fscore[base + j], w.r_fidx[base + j], sc, idx)) {
+            sc = w.r_fscore[base + j];
+            idx = w.r_fidx[base + j];
+          }
+      }
+    } else {
+      const int64_t base = (int64_t)slot * w.ns_b;
+      for (int j = 0; j < w.ns_b; ++j)
+        if (cand_better(w.b_score[base + j], w.b_idx[base + j], sc, idx)) {
+          sc = w.b_score[base + j];
+          idx = w.b_idx[base + j];
+        }
+    }
+    out_token[t] = idx;
+  }
+}
+
+}  // namespace
+
+int row_split_count(int rows, int V, int* chunk) {
+  const int max_split = max(1, (V + 2047) / 2048);
+  int ns = max(1, (2048 + rows - 1) / max(rows, 1));
+  ns = min(ns, max_split);
+  int c = (V + ns - 1) / ns;
+  c = (c + 7) & ~7;
+  ns = (V + c - 1) / c;
+  if (chunk) *chunk = c;
+  return ns;
+}
+
+hipError_t launch_build_rows(int R, int gamma, const int32_t* lengths, const VerifyWs& w,
+                             hipStream_t stream) {
+  hipLaunchKernelGGL(k_build_rows, dim3(1), dim3(1024), 0, stream, R, gamma, lengths, w);
+  return hipGetLastError();
+}
+
+hipError_t launch_target_lse(bool bf16, int R, int gamma, int V, const void* T, const VerifyWs& w,
+                             hipStream_t stream) {
+  const dim3 grid(R * gamma, w.ns_t);
+  if (bf16)
+    hipLaunchKernelGGL(k_target_lse<uint16_t>, grid, dim3(256), 0, stream, gamma, V,
+                       (const uint16_t*)T, w);
+  else
+    hipLaunchKernelGGL(k_target_lse<float>, grid, dim3(256), 0, stream, gamma, V, (const float*)T, w);
+  return hipGetLastError();
+}
+
+hipError_t launch_decide(bool bf16, int R, int gamma, int V, uint64_t seed, const void* T,
+                         const int32_t* tokens, const double* logq, const VerifyWs& w,
+                         int32_t* n_accept, uint8_t* accept_mask, double* lse_t_out,
+                         hipStream_t stream) {
+  if (bf16)
+    hipLaunchKernelGGL(k_decide<uint16_t>, dim3(R), dim3(256), 0, stream, R, gamma, V, seed,
+                       (const uint16_t*)T, tokens, logq, w, n_accept, accept_mask, lse_t_out);
+  else
+    hipLaunchKernelGGL(k_decide<float>, dim3(R), dim3(256), 0, stream, R, gamma, V, seed,
+                       (const float*)T, tokens, logq, w, n_accept, accept_mask, lse_t_out);
+  return hipGetLastError();
+}
+
+hipError_t launch_bonus(bool bf16, int R, int gamma, int V, uint64_t seed, const void* T,
+                        const VerifyWs& w, hipStream_t stream) {
+  const dim3 grid(R, w.ns_b);
+  if (bf16)
+    hipLaunchKernelGGL(k_bonus<uint16_t>, grid, dim3(256), 0, stream, gamma, V, seed,
+                       (const uint16_t*)T, w);
+  else
+    hipLaunchKernelGGL(k_bonus<float>, grid, dim3(256), 0, stream, gamma, V, seed, (const float*)T, w);
+  return hipGetLastError();
+}
+
+hipError_t launch_finalize(int R, int gamma, const VerifyWs& w, float* cstar, int32_t* out_token,
+                           hipStream_t stream) {
+  const int n = max(R * gamma, R);
+  hipLaunchKernelGGL(k_finalize, dim3((n + 255) / 256), dim3(256), 0, stream, R, gamma, w, cstar,
+                     out_token);
+  return hipGetLastError();
+}
+
+}  // namespace dspark

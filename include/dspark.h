@@ -1,0 +1,154 @@
+/*
+ * dspark.h -- C ABI of the MI355X (gfx950) DSpark draft-and-verify hot path.
+ *
+ * Pages cited (titles as published):
+ *   [P1] "DSpark: Confidence-Scheduled Speculative Decoding with
+ *        Semi-Autoregressive Generation 요약 설명" (summary page)
+ *   [P2] "DSpark: Confidence-Scheduled Speculative Decoding with
+ *        Semi-Autoregressive Generation" (notes page, "DSpark 핵심 기술")
+ *
+ * Conventions shared by every entry point
+ *   - Tensor arguments are DEVICE pointers, row-major, owned by the caller.  The
+ *     library keeps no pointer after the work it enqueued has completed and
+ *     allocates no memory on the hot path (scratch comes from the caller's
+ *     workspace, sized by the *_workspace_bytes queries).
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).  Every
+ *     call is asynchronous on it; outputs are valid after the stream syncs.
+ *     Calls on different streams must use different workspaces.
+ *   - Arguments are checked on the host before anything is enqueued.  On error
+ *     the call returns a negative dspark_status, enqueues nothing, leaves the
+ *     outputs untouched and records a message for dspark_last_error().
+ *   - Values the host cannot see (token ids, confidences) are preconditions:
+ *     token ids must lie in [0, V) and confidences in [0, 1]; out-of-range
+ *     values give unspecified results but every memory access stays in bounds
+ *     (token ids are clamped before they index W1).
+ *   - dtype: DSPARK_F32 (binary32) or DSPARK_BF16 (bfloat16 bit patterns) for
+ *     U, T, W1 and W2.  The Markov-head rank must be 256 (the pages' default).
+ *   - Random numbers: Philox4x32-10 (Salmon et al., SC'11) keyed by `seed`,
+ *     counter (v>>2, k, r, stream), word v&3; uniform ((w>>9)+1/2) 2^-23;
+ *     Gumbel -ln(-ln u).  Streams: 0 draft, 1 accept, 2 residual, 3 bonus.
+ *     k is the 1-based block position, r the request index, v the token id.
+ *   - No C++ exception crosses this interface.
+ */
+#ifndef DSPARK_H_
+#define DSPARK_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  DSPARK_OK = 0,
+  DSPARK_ERR_ARG = -1,        /* null pointer or negative / zero size */
+  DSPARK_ERR_SHAPE = -2,      /* unsupported dimension */
+  DSPARK_ERR_DTYPE = -3,      /* unknown dtype */
+  DSPARK_ERR_WORKSPACE = -4,  /* workspace missing, too small or misaligned */
+  DSPARK_ERR_RANGE = -5,      /* host-visible value out of range */
+  DSPARK_ERR_HIP = -6         /* HIP runtime error while enqueuing */
+} dspark_status;
+
+typedef enum { DSPARK_F32 = 0, DSPARK_BF16 = 1 } dspark_dtype;
+
+/* One decoding round's problem: R requests, gamma block positions, vocabulary
+ * V, Markov-head rank, storage dtype and the round's random seed.
+ * Limits: 1 <= R <= 65536, 1 <= gamma <= 64, 1 <= V < 2^26, R*gamma <= 2^20. */
+typedef struct {
+  int32_t R;
+  int32_t gamma;
+  int32_t V;
+  int32_t rank;
+  int32_t dtype;
+  int32_t reserved;  /* must be 0 */
+  uint64_t seed;
+} dspark_problem;
+
+/* Bytes of the packed W2 operand (see dspark_pack_w2). Returns 0 on bad input. */
+size_t dspark_w2_packed_bytes(const dspark_problem* p);
+
+/* Repack the Markov-head factor W2 [rank, V] into the vocabulary-major layout
+ * the kernels stream (a once-per-model weight preparation, not part of a round).
+ * W2p must hold dspark_w2_packed_bytes(p) bytes, 256-byte aligned.
+ *   bf16: 32-token tiles; tile t holds 16 steps x 64 lanes x 8 values, entry
+ *         ((t*16 + s)*64 + l)*8 + e = W2[128*(l/32) + 8*s + e][32*t + pi(l%32)],
+ *         pi(m) = 16*((m>>2)&1) + 4*(m>>3) + (m&3), zero beyond V.
+ *   f32:  W2 transposed, [ceil(V/32)*32, rank], zero rows beyond V. */
+int dspark_pack_w2(const dspark_problem* p, const void* W2, void* W2p, void* stream);
+
+/* Workspace bytes needed by dspark_draft_step and dspark_verify for problem p
+ * (one buffer serves both when they run on one stream). 0 on bad input. */
+size_t dspark_workspace_bytes(const dspark_problem* p);
+
+/* Stage 1 -- Markov-head semi-autoregressive draft sampling.  [P1 §3.1; P2]
+ * For k = 1..gamma and every request r, with x_0 = anchors[r]:
+ *   z_v = U[r,k-1,v] + sum_i W1[x_{k-1}, i] W2[i, v]      (rank-256 bias B_k)
+ *   lse[r,k-1]  = log sum_v exp(z_v)                     (p^d_k = softmax(z))
+ *   x_k         = argmax_v (z_v + Gumbel(stream 0, r, k, v)), lowest v on ties
+ *   logq[r,k-1] = z_{x_k} - lse[r,k-1]                   (log p^d_k(x_k))
+ * U: [R, gamma, V] dtype; W1: [V, 256] dtype; W2p: packed W2; anchors: [R] int32.
+ * Outputs: tokens [R, gamma] int32, lse and logq [R, gamma] float64.
+ * ws: dspark_workspace_bytes(p) bytes, 256-byte aligned. */
+int dspark_draft_step(const dspark_problem* p, const void* U, const void* W1, const void* W2p,
+                      const int32_t* anchors, int32_t* tokens, double* lse, double* logq,
+                      void* ws, size_t ws_bytes, void* stream);
+
+/* Stage 2 -- standard speculative rejection sampling with bonus token, and the
+ * analytic acceptance c*.  [P1 요약, §3.2.1; P2 배경]
+ * For request r with verify length l_r = lengths[r] (all gamma if lengths is
+ * NULL), for k = 1..l_r:
+ *   p^d_k = softmax(U[r,k-1] + W1[x_{k-1}] W2) (recomputed; lse_d from stage 1)
+ *   p^t_k = softmax(T[r,k-1])
+ *   cstar[r,k-1] = sum_v min(p^d_k, p^t_k) = 1 - ||p^d_k - p^t_k||_1 / 2
+ *   accept x_k iff ln u < ln p^t_k(x_k) - logq[r,k-1], u = uniform(stream 1, r, k, v=0)
+ * n_accept[r] = number of leading accepted positions.  If a position k* <= l_r
+ * is rejected, out_token[r] = argmax_v (ln max(0, p^t - p^d)_v + Gumbel(2, r, k*, v))
+ * (falling back to ln p^t if that residual is empty); otherwise out_token[r] =
+ * argmax_v (T[r,l_r,v] + Gumbel(3, r, l_r+1, v)) -- the bonus draw from p^t_{l_r+1}.
+ * T: [R, gamma+1, V] dtype (row gamma is the bonus row).  tokens, lse_d, logq:
+ * stage-1 outputs.  lengths: [R] int32 in [0, gamma] or NULL.
+ * Outputs: cstar [R, gamma] float32 (NaN for k > l_r); n_accept, out_token [R]
+ * int32; accept_mask [R, gamma] uint8 or NULL (1 accepted, 0 rejected, 255 not
+ * decided); lse_t [R, gamma+1] float64 or NULL (NaN where not computed). */
+int dspark_verify(const dspark_problem* p, const void* U, const void* W1, const void* W2p,
+                  const int32_t* anchors, const int32_t* tokens, const double* lse_d,
+                  const double* logq, const void* T, const int32_t* lengths, float* cstar,
+                  int32_t* n_accept, int32_t* out_token, uint8_t* accept_mask, double* lse_t,
+                  void* ws, size_t ws_bytes, void* stream);
+
+/* Confidence head with Sequential Temperature Scaling.  [P1 §3.2.1]
+ * c[r,k-1] = 1 / (1 + exp(-(w . [h[r,k-1,:]; W1[x_{k-1},:]]) / temps[k-1])),
+ * evaluated in float64 and rounded to float32.  h: [R, gamma, H] bfloat16;
+ * w: [H + 256] float32; temps: [gamma] float32 (> 0); W1 [V, 256] in p->dtype;
+ * anchors [R], tokens [R, gamma] int32.  Output c: [R, gamma] float32.
+ * Limits: 1 <= H <= 65536. */
+int dspark_confidence(const dspark_problem* p, int32_t H, const uint16_t* h, const float* w,
+                      const float* temps, const void* W1, const int32_t* anchors,
+                      const int32_t* tokens, float* c, void* stream);
+
+/* Stages 3-4 -- prefix-survival products and the hardware-aware prefix
+ * scheduler (Algorithm 1).  [P1 §3.2.2]
+ *   a[r,j-1] = a[r,j-2] * c[r,j-1] in binary32, a[r,0] = c[r,0]
+ *   candidates (r, j) in order of the key (-a[r,j-1], r, j); start from l = 0,
+ *   B = R, tau = R, Theta = R * sps[R-1]; take candidates while
+ *   Theta' = tau' * sps[B'-1] > Theta (strict), B' = B + 1, tau' = tau + a;
+ *   stop at the first non-improvement (causal).  tau is accumulated exactly in
+ *   units of 2^-38 (each a rounded to nearest-even), Theta = double(tau) * SPS.
+ * c: [R, gamma] float32 in [0, 1]; sps: [n_sps] float32, sps[B-1] = SPS(B),
+ * n_sps >= R*(gamma+1).  Outputs: a [R, gamma] float32; lengths [R] int32;
+ * stats [4] float64 = (B, tau, Theta, n_selected); theta_path [R*gamma+1]
+ * float64 or NULL (Theta before any candidate, then after each examined
+ * candidate up to and including the stopping one, NaN afterwards).
+ * Limit: R*gamma <= 16384.  No workspace is needed. */
+int dspark_schedule(int32_t R, int32_t gamma, const float* c, const float* sps, int32_t n_sps,
+                    float* a, int32_t* lengths, double* stats, double* theta_path, void* stream);
+
+/* Message for the last failing call on this thread ("" if none). */
+const char* dspark_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DSPARK_H_ */

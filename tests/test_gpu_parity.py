@@ -1,0 +1,177 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle, at sizes
+the oracle finishes in seconds (several vocabulary tiles, ragged tails,
+several row blocks), plus edge cases.  Stage-isolated: each GPU stage gets the
+oracle's upstream outputs."""
+import numpy as np
+import pytest
+
+from parity_util import (compare_draft, compare_schedule, compare_verify, build_target,
+                         gen_inputs, log, to_dev)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dev():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from draft_sampling_verification_w1_amd import dspark
+    dspark.lib()
+    return dspark
+
+
+def _run_case(dspark, cfg, lengths=None, check_schedule=True):
+    import torch
+    from oracle import oracle as O
+    from draft_sampling_verification_w1_amd import synth
+    log(f"case {cfg.name} R={cfg.R} gamma={cfg.gamma} V={cfg.V} dtype={cfg.dtype}")
+    inp = gen_inputs(cfg)
+    od = O.draft(inp["U"], inp["W1"], inp["W2"], inp["anchors"], cfg.seed)
+    U, W1, W2 = to_dev(inp["U"]), to_dev(inp["W1"]), to_dev(inp["W2"])
+    anchors = to_dev(inp["anchors"])
+    W2p = dspark.pack_w2(W2, cfg.V)
+    tok, lse, logq = dspark.draft_step(U, W1, W2p, anchors, cfg.seed)
+    torch.cuda.synchronize()
+    n, ties = compare_draft(od, tok.cpu().numpy(), lse.cpu().numpy(), logq.cpu().numpy())
+    log(f"  draft: {n} positions compared, {ties} near-ties")
+
+    T = build_target(cfg, inp, od["tokens"])
+    ov = O.verify(inp["U"], inp["W1"], inp["W2"], inp["anchors"], od["tokens"], T, lengths, cfg.seed)
+    g = dspark.verify(U, W1, W2p, anchors, to_dev(od["tokens"]), to_dev(od["lse"]),
+                      to_dev(od["logq"]), to_dev(T), None if lengths is None else to_dev(lengths),
+                      cfg.seed)
+    torch.cuda.synchronize()
+    gn = {k: (v.cpu().numpy() if v is not None else None) for k, v in g.items()}
+    n, ties = compare_verify(ov, gn)
+    log(f"  verify: {n} requests compared, {ties} near-ties; mean c* {np.nanmean(ov['cstar']):.4f}, "
+        f"mean accepted {ov['n_accept'].mean():.3f}")
+
+    if check_schedule:
+        c = np.nan_to_num(ov["cstar"], nan=0.0).astype(np.float32)
+        a = O.prefix_products(c)
+        sps = synth.sps_table(cfg)
+        os_ = O.schedule(a, sps)
+        os_["a"] = a
+        gs = dspark.schedule(to_dev(c), to_dev(sps))
+        torch.cuda.synchronize()
+        ties = compare_schedule(os_, gs["a"].cpu().numpy(),
+                                {k: v.cpu().numpy() for k, v in gs.items() if k != "a"})
+        log(f"  schedule: n_sel {int(os_['stats'][3])}, B {int(os_['stats'][0])}, ties {ties}")
+
+
+def test_tiny_config(dev):
+    """The tiny fp32 workload (R=4, gamma=8, V=4096) end to end, stage by stage."""
+    from draft_sampling_verification_w1_amd import synth
+    _run_case(dev, synth.CONFIGS["tiny"])
+
+
+@pytest.mark.parametrize("R,gamma,V", [(32, 4, 5000), (40, 3, 4099), (3, 5, 2049), (1, 1, 40),
+                                       (300, 2, 3000), (64, 2, 33)])
+def test_bf16_shapes(dev, R, gamma, V):
+    """bf16 rows on the matrix-core path: ragged vocabularies (not multiples of
+    the 32-token tile, and of the 8-element vector load), several row blocks."""
+    from draft_sampling_verification_w1_amd import synth
+    cfg = synth.scaled(synth.CONFIGS["qwen3_4b"], name=f"bf16_{R}x{gamma}x{V}", R=R, gamma=gamma,
+                       V=V, n_sps=R * (gamma + 1))
+    _run_case(dev, cfg)
+
+
+def test_large_vocab_distributions_small(dev):
+    from draft_sampling_verification_w1_amd import synth
+    cfg = synth.scaled(synth.CONFIGS["large_vocab"], name="lv_small", R=16, gamma=4, V=8192,
+                       n_sps=16 * 5)
+    _run_case(dev, cfg)
+
+
+def test_verify_lengths(dev):
+    """Per-request verify lengths in [0, gamma], including 0 and gamma."""
+    from draft_sampling_verification_w1_amd import synth
+    cfg = synth.scaled(synth.CONFIGS["high_concurrency"], name="lengths", R=24, gamma=6, V=3000,
+                       n_sps=24 * 7)
+    lengths = np.random.default_rng(5).integers(0, 7, 24).astype(np.int32)
+    lengths[:3] = [0, 6, 1]
+    _run_case(dev, cfg, lengths=lengths, check_schedule=False)
+
+
+def test_fp32_ragged(dev):
+    from draft_sampling_verification_w1_amd import synth
+    cfg = synth.scaled(synth.CONFIGS["tiny"], name="f32_ragged", R=7, gamma=3, V=1001, n_sps=28)
+    _run_case(dev, cfg)
+
+
+def test_draft_is_deterministic(dev):
+    import torch
+    from draft_sampling_verification_w1_amd import synth
+    cfg = synth.scaled(synth.CONFIGS["qwen3_4b"], name="det", R=48, gamma=3, V=6000)
+    inp = gen_inputs(cfg)
+    U, W1 = to_dev(inp["U"]), to_dev(inp["W1"])
+    W2p = dev.pack_w2(to_dev(inp["W2"]), cfg.V)
+    a = to_dev(inp["anchors"])
+    r1 = [t.cpu() for t in dev.draft_step(U, W1, W2p, a, 77)]
+    r2 = [t.cpu() for t in dev.draft_step(U, W1, W2p, a, 77)]
+    for x, y in zip(r1, r2):
+        assert torch.equal(x, y)
+    r3 = dev.draft_step(U, W1, W2p, a, 78)[0].cpu()
+    assert not torch.equal(r1[0], r3)
+
+
+def test_pack_layout(dev):
+    """Packed W2 follows the layout documented in include/dspark.h."""
+    import torch
+    V = 100
+    W2 = np.random.default_rng(0).integers(0, 65535, (256, V)).astype(np.uint16)
+    p = dev.pack_w2(to_dev(W2), V).cpu().numpy().view(np.uint16)
+    ntiles = (V + 31) // 32
+    assert p.size == ntiles * 16 * 64 * 8
+    pi = lambda m: 16 * ((m >> 2) & 1) + 4 * (m >> 3) + (m & 3)
+    for t in range(ntiles):
+        for s in range(16):
+            for l in range(64):
+                v = 32 * t + pi(l % 32)
+                for e in range(8):
+                    k = 128 * (l // 32) + 8 * s + e
+                    ref = W2[k, v] if v < V else 0
+                    assert p[((t * 16 + s) * 64 + l) * 8 + e] == ref
+    Wf = np.random.default_rng(1).standard_normal((256, V)).astype(np.float32)
+    pf = dev.pack_w2(to_dev(Wf), V).cpu().numpy().view(np.float32).reshape(ntiles * 32, 256)
+    np.testing.assert_array_equal(pf[:V], Wf.T)
+    assert np.all(pf[V:] == 0)
+
+
+def test_confidence_head(dev):
+    import torch
+    from oracle import oracle as O
+    from draft_sampling_verification_w1_amd import synth
+    cfg = synth.scaled(synth.CONFIGS["full_round"], name="conf", R=10, gamma=5, V=3000)
+    h, w = synth.confidence_inputs(cfg)
+    W1, _ = synth.weights(cfg)
+    anchors = synth.anchors(cfg)
+    tokens = np.random.default_rng(2).integers(0, cfg.V, (cfg.R, cfg.gamma)).astype(np.int32)
+    temps = synth.sts_temperatures(cfg)
+    oc = O.confidence(h, w, temps, W1, anchors, tokens)
+    gc = dev.confidence(to_dev(h), to_dev(w), to_dev(temps), to_dev(W1), to_dev(anchors),
+                        to_dev(tokens)).cpu().numpy()
+    ulp = np.abs(gc.view(np.int32).astype(np.int64) - oc.view(np.int32).astype(np.int64))
+    assert ulp.max() <= 1, f"confidence differs by {ulp.max()} ulp"
+    np.testing.assert_allclose(gc, oc, rtol=1e-6, atol=0)
+
+
+@pytest.mark.parametrize("R,gamma", [(1, 1), (4, 8), (37, 5), (512, 16), (1024, 16)])
+def test_schedule_against_oracle(dev, R, gamma):
+    import torch
+    from oracle import oracle as O
+    from draft_sampling_verification_w1_amd import synth
+    cfg = synth.scaled(synth.CONFIGS["full_round"], name="sched", R=R, gamma=gamma, n_sps=R * (gamma + 1))
+    c = synth.survival_inputs(cfg)
+    c[0, 0] = 1.0
+    if R > 2:
+        c[1] = c[2]                    # equal survival across requests: tie broken by request id
+    a = O.prefix_products(c)
+    for sps in [synth.sps_table(cfg),
+                (1000.0 * np.minimum(1.0, (R + R * gamma // 3) / np.arange(1, R * (gamma + 1) + 1))).astype(np.float32)]:
+        os_ = O.schedule(a, sps)
+        os_["a"] = a
+        gs = dev.schedule(to_dev(c), to_dev(sps))
+        torch.cuda.synchronize()
+        compare_schedule(os_, gs["a"].cpu().numpy(), {k: v.cpu().numpy() for k, v in gs.items() if k != "a"})
