@@ -2,8 +2,12 @@
 // carving and the launch sequence of each stage.  Host code only.
 #include <stdarg.h>
 #include <stdio.h>
+#include <string.h>
 
+#include <map>
+#include <mutex>
 #include <string>
+#include <vector>
 
 #include "dspark.h"
 #include "kernels.h"
@@ -157,9 +161,100 @@ size_t packed_bytes(const dspark_problem* p) {
   return p->dtype == DSPARK_BF16 ? ntiles * kSteps * 64 * 16 : ntiles * kTile * kRank * 4;
 }
 
+// ---- per-kernel timing (tracing) -----------------------------------------
+struct TimingRecord {
+  const char* name;
+  hipEvent_t start, stop;
+};
+
+std::mutex g_timing_mu;
+bool g_timing_on = false;
+std::vector<TimingRecord> g_timing_recs;
+std::vector<hipEvent_t> g_event_pool;
+
+hipEvent_t pooled_event() {
+  if (!g_event_pool.empty()) {
+    hipEvent_t e = g_event_pool.back();
+    g_event_pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+void recycle_records() {
+  for (auto& r : g_timing_recs) {
+    g_event_pool.push_back(r.start);
+    g_event_pool.push_back(r.stop);
+  }
+  g_timing_recs.clear();
+}
+
 }  // namespace
 
+namespace dspark {
+
+TimingScope::TimingScope(const char* name, hipStream_t stream) : slot_(-1), stream_(stream) {
+  std::lock_guard<std::mutex> lock(g_timing_mu);
+  if (!g_timing_on) return;
+  TimingRecord r{name, pooled_event(), pooled_event()};
+  if (!r.start || !r.stop || hipEventRecord(r.start, stream) != hipSuccess) return;
+  g_timing_recs.push_back(r);
+  slot_ = (int)g_timing_recs.size() - 1;
+}
+
+TimingScope::~TimingScope() {
+  if (slot_ < 0) return;
+  std::lock_guard<std::mutex> lock(g_timing_mu);
+  if (slot_ < (int)g_timing_recs.size()) hipEventRecord(g_timing_recs[slot_].stop, stream_);
+}
+
+}  // namespace dspark
+
 extern "C" {
+
+__attribute__((visibility("default"))) int dspark_timing_enable(int on) {
+  std::lock_guard<std::mutex> lock(g_timing_mu);
+  if (on) recycle_records();
+  g_timing_on = on != 0;
+  return ok();
+}
+
+__attribute__((visibility("default"))) int dspark_timing_report(char* buf, size_t cap) {
+  std::lock_guard<std::mutex> lock(g_timing_mu);
+  std::map<std::string, std::pair<long, double>> agg;
+  std::vector<std::string> order;
+  for (auto& r : g_timing_recs) {
+    hipError_t e = hipEventSynchronize(r.stop);
+    if (e != hipSuccess) return hip_fail(e, "timing report");
+    float ms = 0.f;
+    e = hipEventElapsedTime(&ms, r.start, r.stop);
+    if (e != hipSuccess) return hip_fail(e, "timing report");
+    auto it = agg.find(r.name);
+    if (it == agg.end()) {
+      order.push_back(r.name);
+      agg[r.name] = {1, ms};
+    } else {
+      it->second.first += 1;
+      it->second.second += ms;
+    }
+  }
+  std::string out;
+  char line[256];
+  for (auto& name : order) {
+    snprintf(line, sizeof line, "%s %ld %.6f\n", name.c_str(), agg[name].first, agg[name].second);
+    out += line;
+  }
+  if (buf && cap) {  // a size query (buf NULL) keeps the record
+    recycle_records();
+    const size_t n = out.size() < cap - 1 ? out.size() : cap - 1;
+    memcpy(buf, out.data(), n);
+    buf[n] = '\0';
+  }
+  g_last_error.clear();
+  return (int)out.size();
+}
 
 __attribute__((visibility("default"))) const char* dspark_last_error(void) {
   return g_last_error.c_str();

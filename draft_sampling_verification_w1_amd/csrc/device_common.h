@@ -27,15 +27,23 @@ constexpr uint32_t kStreamDraft = 0, kStreamAccept = 1, kStreamResidual = 2, kSt
 // 32x32->64 multiplies, a word permutation and a key xor; the key advances by
 // the Weyl increments between rounds.
 // ---------------------------------------------------------------------------
+// Three-input xor in one gfx950 v_bitop3_b32 (truth table 0x96); the third
+// operand is the wave-uniform round key, read straight from an SGPR.
+__device__ __forceinline__ uint32_t xor3(uint32_t a, uint32_t b, uint32_t key) {
+  uint32_t r;
+  asm("v_bitop3_b32 %0, %1, %2, %3 bitop3:0x96" : "=v"(r) : "v"(a), "v"(b), "s"(key));
+  return r;
+}
+
 __device__ __forceinline__ u32x4 philox4x32_10(u32x4 x, uint32_t k0, uint32_t k1) {
 #pragma unroll
   for (int round = 0; round < 10; ++round) {
     const uint64_t lo_hi0 = (uint64_t)0xD2511F53u * (uint64_t)x.x;
     const uint64_t lo_hi1 = (uint64_t)0xCD9E8D57u * (uint64_t)x.z;
     u32x4 y;
-    y.x = (uint32_t)(lo_hi1 >> 32) ^ x.y ^ k0;
+    y.x = xor3((uint32_t)(lo_hi1 >> 32), x.y, k0);
     y.y = (uint32_t)lo_hi1;
-    y.z = (uint32_t)(lo_hi0 >> 32) ^ x.w ^ k1;
+    y.z = xor3((uint32_t)(lo_hi0 >> 32), x.w, k1);
     y.w = (uint32_t)lo_hi0;
     x = y;
     k0 += 0x9E3779B9u;
@@ -59,9 +67,11 @@ __device__ __forceinline__ uint32_t word_of(u32x4 b, int i) {
   return i == 0 ? b.x : (i == 1 ? b.y : (i == 2 ? b.z : b.w));
 }
 
-// Uniform ((w>>9) + 1/2) 2^-23, exact in binary32.
+// Uniform ((w>>9) + 1/2) 2^-23, exact in binary32: the top 23 bits become the
+// mantissa of f in [1, 2) (one v_alignbit), and f - (1 - 2^-24) is exact.
 __device__ __forceinline__ float uniform_f32(uint32_t w) {
-  return fmaf((float)(w >> 9), 0x1p-23f, 0x1p-24f);
+  const float f = __uint_as_float(__builtin_amdgcn_alignbit(0x7Fu, w, 9));
+  return f - 0x1.fffffep-1f;
 }
 
 __device__ __forceinline__ double uniform_f64(uint32_t w) {

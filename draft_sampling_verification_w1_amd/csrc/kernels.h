@@ -13,6 +13,18 @@ constexpr int kSteps = kRank / 16;
 
 enum BiasMode { kModeDraft = 0, kModeCstar = 1, kModeResidual = 2 };
 
+// Brackets one kernel launch with HIP events when library timing is enabled
+// (dspark_timing_enable); a no-op otherwise.
+class TimingScope {
+ public:
+  TimingScope(const char* name, hipStream_t stream);
+  ~TimingScope();
+
+ private:
+  int slot_;
+  hipStream_t stream_;
+};
+
 // Arguments of one split-vocabulary pass over a set of (request, position)
 // rows: bias B = W1[x_{k-1}] W2 plus backbone logits U, consumed by a
 // mode-specific epilogue.  Partial records are indexed [row * nsplit + split].

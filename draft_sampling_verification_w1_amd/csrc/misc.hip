@@ -67,6 +67,7 @@ __global__ __launch_bounds__(256) void k_confidence(int R, int gamma, int V, int
 }  // namespace
 
 hipError_t launch_pack_w2(bool bf16, int V, const void* W2, void* W2p, hipStream_t stream) {
+  TimingScope timing("pack_w2", stream);
   const int ntiles = (V + kTile - 1) / kTile;
   if (bf16) {
     const int64_t n = (int64_t)ntiles * kSteps * 64;
@@ -84,6 +85,7 @@ hipError_t launch_confidence(bool w1_bf16, int R, int gamma, int V, int H, const
                              const float* w, const float* temps, const void* W1,
                              const int32_t* anchors, const int32_t* tokens, float* c,
                              hipStream_t stream) {
+  TimingScope timing("confidence", stream);
   const int rows = R * gamma;
   const dim3 grid((rows + 3) / 4);
   if (w1_bf16)

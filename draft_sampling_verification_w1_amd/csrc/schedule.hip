@@ -134,6 +134,7 @@ __global__ __launch_bounds__(kThreads) void k_schedule(int R, int gamma, const f
 hipError_t launch_schedule(int R, int gamma, const float* c, const float* sps, float* a,
                            int32_t* lengths, double* stats, double* theta_path,
                            hipStream_t stream) {
+  TimingScope timing("schedule", stream);
   hipLaunchKernelGGL(k_schedule, dim3(1), dim3(kThreads), 0, stream, R, gamma, c, sps, a, lengths,
                      stats, theta_path);
   return hipGetLastError();

@@ -273,50 +273,72 @@ __global__ __launch_bounds__(256) void k_bonus(int gamma, int V, uint64_t seed, 
   }
 }
 
+__device__ __forceinline__ void wave_best(double& sc, int& idx) {
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const double s2 = __shfl_xor(sc, off, 64);
+    const int i2 = __shfl_xor(idx, off, 64);
+    if (cand_better(s2, i2, sc, idx)) {
+      sc = s2;
+      idx = i2;
+    }
+  }
+}
+
+// One wave per verified-position entry (c* sum over the vocabulary splits),
+// then one wave per request (corrective or bonus token over its splits).
 __global__ __launch_bounds__(256) void k_finalize(int R, int gamma, VerifyWs w, float* cstar,
                                                   int32_t* out_token) {
-  const int t = blockIdx.x * 256 + threadIdx.x;
-  if (t < R * gamma) {
-    const int r = t / gamma;
-    const int k = t - r * gamma + 1;
-    float c = NAN;
-    if (k <= w.req_len[r]) {
-      const int64_t base = (int64_t)(w.req_off[r] + k - 1) * w.ns_c;
-      double s = 0.0;
-      for (int j = 0; j < w.ns_c; ++j) s += w.c_s[base + j];
-      c = (float)s;
+  const int lane = threadIdx.x & 63;
+  const int item = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int n_c = R * gamma;
+  if (item < n_c) {
+    const int r = item / gamma;
+    const int k = item - r * gamma + 1;
+    if (k > w.req_len[r]) {
+      if (lane == 0) cstar[item] = NAN;
+      return;
     }
-    cstar[t] = c;
+    const int64_t base = (int64_t)(w.req_off[r] + k - 1) * w.ns_c;
+    double s = 0.0;
+    for (int j = lane; j < w.ns_c; j += 64) s += w.c_s[base + j];
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) s += __shfl_xor(s, off, 64);
+    if (lane == 0) cstar[item] = (float)s;
+    return;
   }
-  if (t < R) {
-    const int slot = w.req_slot[t];
-    double sc = -INFINITY;
-    int idx = -1;
-    if (w.req_mode[t] == 1) {
-      const int64_t base = (int64_t)slot * w.ns_r;
-      for (int j = 0; j < w.ns_r; ++j)
-        if (cand_better(w.r_score[base + j], w.r_idx[base + j], sc, idx)) {
-          sc = w.r_score[base + j];
-          idx = w.r_idx[base + j];
-        }
-      if (idx < 0) {  // empty residual after rounding: draw from p^t instead
-        sc = -INFINITY;
-        for (int j = 0; j < w.ns_r; ++j)
-          if (cand_better(w.r_fscore[base + j], w.r_fidx[base + j], sc, idx)) {
-            sc = w.r_fscore[base + j];
-            idx = w.r_fidx[base + j];
-          }
+  const int r = item - n_c;
+  if (r >= R) return;
+  const int slot = w.req_slot[r];
+  double sc = -INFINITY;
+  int idx = -1;
+  if (w.req_mode[r] == 1) {
+    const int64_t base = (int64_t)slot * w.ns_r;
+    for (int j = lane; j < w.ns_r; j += 64)
+      if (cand_better(w.r_score[base + j], w.r_idx[base + j], sc, idx)) {
+        sc = w.r_score[base + j];
+        idx = w.r_idx[base + j];
       }
-    } else {
-      const int64_t base = (int64_t)slot * w.ns_b;
-      for (int j = 0; j < w.ns_b; ++j)
-        if (cand_better(w.b_score[base + j], w.b_idx[base + j], sc, idx)) {
-          sc = w.b_score[base + j];
-          idx = w.b_idx[base + j];
+    wave_best(sc, idx);
+    if (idx < 0) {  // empty residual after rounding: draw from p^t instead
+      sc = -INFINITY;
+      for (int j = lane; j < w.ns_r; j += 64)
+        if (cand_better(w.r_fscore[base + j], w.r_fidx[base + j], sc, idx)) {
+          sc = w.r_fscore[base + j];
+          idx = w.r_fidx[base + j];
         }
+      wave_best(sc, idx);
     }
-    out_token[t] = idx;
+  } else {
+    const int64_t base = (int64_t)slot * w.ns_b;
+    for (int j = lane; j < w.ns_b; j += 64)
+      if (cand_better(w.b_score[base + j], w.b_idx[base + j], sc, idx)) {
+        sc = w.b_score[base + j];
+        idx = w.b_idx[base + j];
+      }
+    wave_best(sc, idx);
   }
+  if (lane == 0) out_token[r] = idx;
 }
 
 }  // namespace
@@ -334,12 +356,14 @@ int row_split_count(int rows, int V, int* chunk) {
 
 hipError_t launch_build_rows(int R, int gamma, const int32_t* lengths, const VerifyWs& w,
                              hipStream_t stream) {
+  TimingScope timing("build_rows", stream);
   hipLaunchKernelGGL(k_build_rows, dim3(1), dim3(1024), 0, stream, R, gamma, lengths, w);
   return hipGetLastError();
 }
 
 hipError_t launch_target_lse(bool bf16, int R, int gamma, int V, const void* T, const VerifyWs& w,
                              hipStream_t stream) {
+  TimingScope timing("target_lse", stream);
   const dim3 grid(R * gamma, w.ns_t);
   if (bf16)
     hipLaunchKernelGGL(k_target_lse<uint16_t>, grid, dim3(256), 0, stream, gamma, V,
@@ -353,6 +377,7 @@ hipError_t launch_decide(bool bf16, int R, int gamma, int V, uint64_t seed, cons
                          const int32_t* tokens, const double* logq, const VerifyWs& w,
                          int32_t* n_accept, uint8_t* accept_mask, double* lse_t_out,
                          hipStream_t stream) {
+  TimingScope timing("decide", stream);
   if (bf16)
     hipLaunchKernelGGL(k_decide<uint16_t>, dim3(R), dim3(256), 0, stream, R, gamma, V, seed,
                        (const uint16_t*)T, tokens, logq, w, n_accept, accept_mask, lse_t_out);
@@ -364,6 +389,7 @@ hipError_t launch_decide(bool bf16, int R, int gamma, int V, uint64_t seed, cons
 
 hipError_t launch_bonus(bool bf16, int R, int gamma, int V, uint64_t seed, const void* T,
                         const VerifyWs& w, hipStream_t stream) {
+  TimingScope timing("bonus", stream);
   const dim3 grid(R, w.ns_b);
   if (bf16)
     hipLaunchKernelGGL(k_bonus<uint16_t>, grid, dim3(256), 0, stream, gamma, V, seed,
@@ -375,8 +401,9 @@ hipError_t launch_bonus(bool bf16, int R, int gamma, int V, uint64_t seed, const
 
 hipError_t launch_finalize(int R, int gamma, const VerifyWs& w, float* cstar, int32_t* out_token,
                            hipStream_t stream) {
-  const int n = max(R * gamma, R);
-  hipLaunchKernelGGL(k_finalize, dim3((n + 255) / 256), dim3(256), 0, stream, R, gamma, w, cstar,
+  TimingScope timing("finalize", stream);
+  const int waves = R * gamma + R;
+  hipLaunchKernelGGL(k_finalize, dim3((waves + 3) / 4), dim3(256), 0, stream, R, gamma, w, cstar,
                      out_token);
   return hipGetLastError();
 }

@@ -20,7 +20,7 @@ _DTYPES = {torch.float32: F32, torch.bfloat16: BF16}
 
 SYMBOLS = ("dspark_w2_packed_bytes", "dspark_pack_w2", "dspark_workspace_bytes",
            "dspark_draft_step", "dspark_verify", "dspark_confidence", "dspark_schedule",
-           "dspark_last_error")
+           "dspark_last_error", "dspark_timing_enable", "dspark_timing_report")
 
 
 class Problem(ctypes.Structure):
@@ -59,8 +59,10 @@ def lib() -> ctypes.CDLL:
         L.dspark_schedule.argtypes = [ctypes.c_int32, ctypes.c_int32, _vp, _vp, ctypes.c_int32, _vp,
                                       _vp, _vp, _vp, _vp]
         L.dspark_last_error.restype = ctypes.c_char_p
+        L.dspark_timing_enable.argtypes = [ctypes.c_int]
+        L.dspark_timing_report.argtypes = [ctypes.c_char_p, ctypes.c_size_t]
         for name in ("dspark_pack_w2", "dspark_draft_step", "dspark_verify", "dspark_confidence",
-                     "dspark_schedule"):
+                     "dspark_schedule", "dspark_timing_enable", "dspark_timing_report"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -145,10 +147,32 @@ def draft_step(U, W1, W2p, anchors, seed: int, ws=None, out=None):
     return tokens, lse, logq
 
 
+def timing_enable(on: bool = True):
+    """Start (clearing the record) or stop per-kernel HIP-event timing."""
+    _check(lib().dspark_timing_enable(1 if on else 0))
+
+
+def timing_report() -> dict:
+    """{kernel name: (launches, total ms)} of the recorded launches; clears the record."""
+    n = lib().dspark_timing_report(None, 0)
+    if n < 0:
+        _check(n)
+    buf = ctypes.create_string_buffer(n + 1)
+    n = lib().dspark_timing_report(buf, n + 1)
+    if n < 0:
+        _check(n)
+    out = {}
+    for line in buf.value.decode().splitlines():
+        name, cnt, ms = line.split()
+        out[name] = (int(cnt), float(ms))
+    return out
+
+
 def verify(U, W1, W2p, anchors, tokens, lse_d, logq, T, lengths, seed: int, ws=None,
-           with_mask: bool = True, with_lse_t: bool = True):
+           with_mask: bool = True, with_lse_t: bool = True, out=None):
     """Stage 2 (dspark_verify).  Returns dict of cstar, n_accept, out_token,
-    accept_mask (optional) and lse_t (optional)."""
+    accept_mask (optional) and lse_t (optional); ``out`` may supply that dict
+    preallocated."""
     R, gamma, V = U.shape
     _need(U, "U")
     _need(T, "T", dtype=U.dtype, shape=(R, gamma + 1, V))
@@ -164,7 +188,7 @@ def verify(U, W1, W2p, anchors, tokens, lse_d, logq, T, lengths, seed: int, ws=N
     if ws is None:
         ws = workspace(p, U.device)
     dev = U.device
-    out = {
+    out = out if out is not None else {
         "cstar": torch.empty((R, gamma), dtype=torch.float32, device=dev),
         "n_accept": torch.empty(R, dtype=torch.int32, device=dev),
         "out_token": torch.empty(R, dtype=torch.int32, device=dev),
@@ -196,16 +220,20 @@ def confidence(h, w, temps, W1, anchors, tokens, seed: int = 0):
     return c
 
 
-def schedule(c, sps, with_path: bool = True):
-    """Stages 3-4 (dspark_schedule).  c [R, gamma] fp32, sps [n] fp32."""
+def schedule(c, sps, with_path: bool = True, out=None):
+    """Stages 3-4 (dspark_schedule).  c [R, gamma] fp32, sps [n] fp32; ``out``
+    may supply the result dict preallocated."""
     R, gamma = c.shape
     _need(c, "c", dtype=torch.float32)
     _need(sps, "sps", dtype=torch.float32)
     dev = c.device
-    a = torch.empty((R, gamma), dtype=torch.float32, device=dev)
-    lengths = torch.empty(R, dtype=torch.int32, device=dev)
-    stats = torch.empty(4, dtype=torch.float64, device=dev)
-    path = torch.empty(R * gamma + 1, dtype=torch.float64, device=dev) if with_path else None
-    _check(lib().dspark_schedule(R, gamma, _ptr(c), _ptr(sps), sps.numel(), _ptr(a), _ptr(lengths),
-                                 _ptr(stats), _ptr(path), _stream()))
-    return {"a": a, "lengths": lengths, "stats": stats, "theta_path": path}
+    if out is None:
+        out = {"a": torch.empty((R, gamma), dtype=torch.float32, device=dev),
+               "lengths": torch.empty(R, dtype=torch.int32, device=dev),
+               "stats": torch.empty(4, dtype=torch.float64, device=dev),
+               "theta_path": torch.empty(R * gamma + 1, dtype=torch.float64, device=dev)
+               if with_path else None}
+    _check(lib().dspark_schedule(R, gamma, _ptr(c), _ptr(sps), sps.numel(), _ptr(out["a"]),
+                                 _ptr(out["lengths"]), _ptr(out["stats"]), _ptr(out["theta_path"]),
+                                 _stream()))
+    return out

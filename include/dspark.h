@@ -147,6 +147,18 @@ int dspark_schedule(int32_t R, int32_t gamma, const float* c, const float* sps, 
 /* Message for the last failing call on this thread ("" if none). */
 const char* dspark_last_error(void);
 
+/* Per-kernel timing with HIP events (tracing; off by default).
+ * dspark_timing_enable(1) clears the record and brackets every kernel the
+ * library enqueues from then on with a pair of events on that kernel's
+ * stream; dspark_timing_enable(0) stops recording.  dspark_timing_report
+ * waits for the recorded events and writes one line per kernel name,
+ * "name launches total_ms\n", into buf (NUL-terminated, truncated to cap),
+ * then clears the record; with buf NULL it only returns the size and keeps
+ * the record.  Returns the bytes needed (excluding the NUL) or a negative
+ * dspark_status. */
+int dspark_timing_enable(int on);
+int dspark_timing_report(char* buf, size_t cap);
+
 #ifdef __cplusplus
 }
 #endif
