@@ -20,7 +20,15 @@
  * Random numbers (READING, pages silent): Philox4x32-10 as defined by Salmon,
  * Moraes, Dror and Shaw, "Parallel Random Numbers: As Easy as 1, 2, 3" (SC'11),
  * keyed by the 64-bit seed, with counter (v>>2, k, r, stream) and word v&3.
- * Streams: 0 draft Gumbel, 1 accept uniform, 2 residual Gumbel, 3 bonus Gumbel.
+ * Streams: 0/4 draft Gumbel (block/member), 1 accept uniform, 2/6 residual
+ * Gumbel (block/member), 3/7 bonus Gumbel (block/member).
+ *
+ * Categorical draws (READING, the pages only say that tokens are sampled from
+ * the distributions): two-level Gumbel-max.  The vocabulary is cut into
+ * consecutive blocks of 32 entries (the last may be shorter); a block is
+ * chosen by Gumbel-max over the blocks' log-masses, then a member of that
+ * block by Gumbel-max over its log-weights.  The law of the draw is exactly
+ * P(block) P(v | block) = softmax(w)_v.
  */
 #include <math.h>
 #include <stdint.h>
@@ -28,6 +36,9 @@
 #include <string.h>
 
 #define ORACLE_API __attribute__((visibility("default")))
+
+/* Entries per sampling block of the two-level Gumbel-max draw (READING). */
+#define ORACLE_SAMPLE_BLOCK 32
 
 /* ------------------------------------------------------------------------ */
 /* Counter-based random numbers (Philox4x32-10, SC'11).                      */
@@ -124,6 +135,42 @@ ORACLE_API int64_t oracle_gumbel_argmax(int64_t n, const double* w, const double
   return best;
 }
 
+/* Two-level Gumbel-max draw from softmax(w) over n entries (w may hold -inf,
+ * at least one entry finite).  Level 1: block b (entries [b*block,
+ * min((b+1)*block, n))) scores logsumexp(w over the block) plus the Gumbel
+ * variate of element b of stream `stream_block`; the best block wins (lowest
+ * b on exact ties).  Level 2: inside the winning block, entry v scores
+ * w_v plus the Gumbel variate of element v of stream `stream_member`.
+ * margin = the smaller of the two levels' top-2 gaps. */
+ORACLE_API int64_t oracle_two_level_draw(int64_t n, const double* w, int64_t block,
+                                         uint64_t seed, uint32_t stream_block,
+                                         uint32_t stream_member, uint32_t r, uint32_t k,
+                                         double* margin) {
+  const int64_t nb = (n + block - 1) / block;
+  double* lb = (double*)malloc((size_t)nb * sizeof(double));
+  double* gb = (double*)malloc((size_t)nb * sizeof(double));
+  for (int64_t b = 0; b < nb; ++b) {
+    const int64_t v0 = b * block;
+    const int64_t len = (v0 + block <= n) ? block : n - v0;
+    lb[b] = oracle_logsumexp(len, w + v0);
+    gb[b] = oracle_gumbel(oracle_word(seed, stream_block, r, k, (uint32_t)b));
+  }
+  double m1, m2;
+  const int64_t bstar = oracle_gumbel_argmax(nb, lb, gb, &m1);
+  const int64_t v0 = bstar * block;
+  const int64_t len = (v0 + block <= n) ? block : n - v0;
+  double g[64];
+  double* gm = len <= 64 ? g : (double*)malloc((size_t)len * sizeof(double));
+  for (int64_t i = 0; i < len; ++i)
+    gm[i] = oracle_gumbel(oracle_word(seed, stream_member, r, k, (uint32_t)(v0 + i)));
+  const int64_t x = v0 + oracle_gumbel_argmax(len, w + v0, gm, &m2);
+  if (gm != g) free(gm);
+  free(lb);
+  free(gb);
+  if (margin) *margin = m1 < m2 ? m1 : m2;
+  return x;
+}
+
 /* Standard speculative acceptance: accept draft token x with probability
  * min(1, p^t(x)/p^d(x)); with u uniform, accept iff u < p^t(x)/p^d(x), taken
  * in log space as ln u < ln p^t(x) - ln p^d(x).  [P1 요약; P2 배경, step 3]
@@ -170,17 +217,14 @@ ORACLE_API void oracle_draft_rows(int64_t nrows, int64_t V, const double* z,
 #pragma omp parallel for schedule(dynamic, 1)
   for (int64_t i = 0; i < nrows; ++i) {
     const double* zi = z + i * V;
-    double* g = (double*)malloc((size_t)V * sizeof(double));
-    for (int64_t v = 0; v < V; ++v)
-      g[v] = oracle_gumbel(oracle_word(seed, 0u, (uint32_t)r_idx[i], (uint32_t)k_idx[i], (uint32_t)v));
     const double l = oracle_logsumexp(V, zi);
     double mg;
-    const int64_t x = oracle_gumbel_argmax(V, zi, g, &mg);
+    const int64_t x = oracle_two_level_draw(V, zi, ORACLE_SAMPLE_BLOCK, seed, 0u, 4u,
+                                            (uint32_t)r_idx[i], (uint32_t)k_idx[i], &mg);
     token[i] = (int32_t)x;
     lse[i] = l;
     logq[i] = zi[x] - l;
     if (margin) margin[i] = mg;
-    free(g);
   }
 }
 
@@ -213,7 +257,6 @@ ORACLE_API void oracle_verify_requests(int64_t nreq, int64_t gamma, int64_t V,
     double* lpd = (double*)malloc((size_t)V * sizeof(double));
     double* lpt = (double*)malloc((size_t)V * sizeof(double));
     double* w = (double*)malloc((size_t)V * sizeof(double));
-    double* g = (double*)malloc((size_t)V * sizeof(double));
     for (int64_t k = 0; k < gamma; ++k) {
       cstar[q * gamma + k] = NAN;
       accept_mask[q * gamma + k] = 255;
@@ -265,16 +308,12 @@ ORACLE_API void oracle_verify_requests(int64_t nreq, int64_t gamma, int64_t V,
       const int64_t positive = oracle_residual_logw(V, lpd, lpt, w);
       if (positive == 0)  /* READING: empty residual after rounding -> p^t */
         for (int64_t v = 0; v < V; ++v) w[v] = lpt[v];
-      for (int64_t v = 0; v < V; ++v)
-        g[v] = oracle_gumbel(oracle_word(seed, 2u, r, (uint32_t)kstar, (uint32_t)v));
-      y = oracle_gumbel_argmax(V, w, g, &mg);
+      y = oracle_two_level_draw(V, w, ORACLE_SAMPLE_BLOCK, seed, 2u, 6u, r, (uint32_t)kstar, &mg);
     } else {
       /* bonus token from p^t at position len+1 (row index len) */
       const int64_t b = len + 1;
       const double* ztb = zt + (q * (gamma + 1) + (b - 1)) * V;
-      for (int64_t v = 0; v < V; ++v)
-        g[v] = oracle_gumbel(oracle_word(seed, 3u, r, (uint32_t)b, (uint32_t)v));
-      y = oracle_gumbel_argmax(V, ztb, g, &mg);
+      y = oracle_two_level_draw(V, ztb, ORACLE_SAMPLE_BLOCK, seed, 3u, 7u, r, (uint32_t)b, &mg);
     }
     n_accept[q] = (int32_t)n;
     out_token[q] = (int32_t)y;
@@ -282,7 +321,6 @@ ORACLE_API void oracle_verify_requests(int64_t nreq, int64_t gamma, int64_t V,
     free(lpd);
     free(lpt);
     free(w);
-    free(g);
   }
 }
 

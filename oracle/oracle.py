@@ -31,6 +31,9 @@ _SRC = os.path.join(_HERE, "dspark_oracle.c")
 _LIB_PATH = os.path.join(_HERE, "liboracle.so")
 _lib = None
 
+#: entries per block of the two-level Gumbel-max draws
+SAMPLE_BLOCK = 32
+
 _f64p = ctypes.POINTER(ctypes.c_double)
 _f32p = ctypes.POINTER(ctypes.c_float)
 _i32p = ctypes.POINTER(ctypes.c_int32)
@@ -68,6 +71,10 @@ def lib() -> ctypes.CDLL:
         L.oracle_logsumexp.restype = ctypes.c_double
         L.oracle_gumbel_argmax.argtypes = [ctypes.c_int64, _f64p, _f64p, _f64p]
         L.oracle_gumbel_argmax.restype = ctypes.c_int64
+        L.oracle_two_level_draw.argtypes = [ctypes.c_int64, _f64p, ctypes.c_int64,
+                                            ctypes.c_uint64, ctypes.c_uint32, ctypes.c_uint32,
+                                            ctypes.c_uint32, ctypes.c_uint32, _f64p]
+        L.oracle_two_level_draw.restype = ctypes.c_int64
         L.oracle_accept.argtypes = [ctypes.c_double, ctypes.c_double, ctypes.c_double]
         L.oracle_accept.restype = ctypes.c_int
         L.oracle_residual_logw.argtypes = [ctypes.c_int64, _f64p, _f64p, _f64p]
@@ -153,6 +160,16 @@ def gumbel_argmax(w, g):
     g = np.ascontiguousarray(g, dtype=np.float64)
     m = ctypes.c_double()
     idx = lib().oracle_gumbel_argmax(w.size, _p(w, _f64p), _p(g, _f64p), ctypes.byref(m))
+    return int(idx), float(m.value)
+
+
+def two_level_draw(w, block: int, seed: int, stream_block: int, stream_member: int,
+                   r: int, k: int):
+    """Two-level Gumbel-max draw from softmax(w): returns (index, margin)."""
+    w = np.ascontiguousarray(w, dtype=np.float64)
+    m = ctypes.c_double()
+    idx = lib().oracle_two_level_draw(w.size, _p(w, _f64p), block, seed, stream_block,
+                                      stream_member, r, k, ctypes.byref(m))
     return int(idx), float(m.value)
 
 

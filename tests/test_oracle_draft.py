@@ -134,3 +134,82 @@ def test_draft_positions_use_their_own_noise(oracle):
     W = np.zeros((V, 4), np.float32)
     out = oracle.draft(U, W, np.zeros((4, V), np.float32), np.zeros(R, np.int32), seed=9)
     assert len(set(out["tokens"].ravel().tolist())) > 10
+
+
+# ---------------------------------------------------------------------------
+# Two-level Gumbel-max (the sampler behind every categorical draw).
+# ---------------------------------------------------------------------------
+def _law_counts(oracle, w, block, n, seed=21):
+    counts = np.zeros(w.size, np.int64)
+    for r in range(n):
+        idx, margin = oracle.two_level_draw(w, block, seed, 0, 4, r, 1)
+        assert margin >= 0
+        counts[idx] += 1
+    return counts
+
+
+@pytest.mark.parametrize("block", [1, 3, 32])
+def test_two_level_draw_has_softmax_law(oracle, block):
+    """P(block) P(v | block) = softmax(w)_v: chi-square over 70 entries in
+    blocks of very different mass (a block scored by its maximum instead of
+    its log-mass, or a shared noise word between the levels, fails this)."""
+    rng = np.random.default_rng(7)
+    w = rng.standard_normal(70) * 1.5
+    w[5:9] = -np.inf            # entries with zero weight are never drawn
+    w[40:43] += 2.5             # one heavy stretch inside a block
+    n = 40_000
+    counts = _law_counts(oracle, w, block, n)
+    p = special.softmax(w)
+    assert counts[5:9].sum() == 0
+    keep = p > 0
+    assert stats.chisquare(counts[keep], n * p[keep]).pvalue > 1e-4
+
+
+def test_two_level_draw_single_block_is_flat_gumbel_max(oracle):
+    """With every block but one at -inf the first level is forced, and the draw
+    is the textbook Gumbel-max over that block with the member stream's words."""
+    rng = np.random.default_rng(8)
+    V, block = 200, 32
+    for trial in range(20):
+        b = int(rng.integers(0, (V + block - 1) // block))
+        w = np.full(V, -np.inf)
+        lo, hi = b * block, min(V, (b + 1) * block)
+        w[lo:hi] = rng.standard_normal(hi - lo) * 2
+        words = oracle.words(3, 4, trial, 2, lo, hi - lo)
+        u = ((words >> 9).astype(np.float64) + 0.5) * 2.0 ** -23
+        expect = lo + int(np.argmax(w[lo:hi] - np.log(-np.log(u))))
+        idx, _ = oracle.two_level_draw(w, block, 3, 0, 4, trial, 2)
+        assert idx == expect
+
+
+def test_two_level_draw_block_choice_uses_block_words(oracle):
+    """With equal mass in every block (a constant w) the block is the argmax of
+    the block stream's Gumbel variates alone."""
+    V, block = 320, 32
+    w = np.zeros(V)
+    for r in range(20):
+        words = oracle.words(5, 0, r, 3, 0, V // block)
+        u = ((words >> 9).astype(np.float64) + 0.5) * 2.0 ** -23
+        b = int(np.argmax(-np.log(-np.log(u))))
+        idx, _ = oracle.two_level_draw(w, block, 5, 0, 4, r, 3)
+        assert idx // block == b
+
+
+def test_two_level_draw_shift_invariant(oracle):
+    rng = np.random.default_rng(9)
+    w = rng.standard_normal(150) * 3
+    for r in range(30):
+        i1, m1 = oracle.two_level_draw(w, 32, 2, 0, 4, r, 1)
+        i2, _ = oracle.two_level_draw(w + 0.75, 32, 2, 0, 4, r, 1)
+        if m1 > 1e-9:
+            assert i1 == i2
+
+
+def test_draft_rows_law_across_blocks(oracle):
+    """The draft stage draws from softmax(z) over a vocabulary of several blocks."""
+    rng = np.random.default_rng(10)
+    z = rng.standard_normal(100) * 1.2
+    n = 60_000
+    t, l, q, m = _draft_rows(oracle, np.tile(z, (n, 1)), 13, np.arange(n), np.full(n, 2))
+    counts = np.bincount(t, minlength=z.size)
+    assert stats.chisquare(counts, n * special.softmax(z)).pvalue > 1e-4
