@@ -66,39 +66,61 @@ struct Carver {
   }
 };
 
+struct CandLayout {
+  size_t lo, hi1, b1, hi2;
+};
+
+CandLayout take_cands(Carver& c, size_t n) {
+  CandLayout L;
+  L.lo = c.take(n * sizeof(float));
+  L.hi1 = c.take(n * sizeof(float));
+  L.b1 = c.take(n * sizeof(int32_t));
+  L.hi2 = c.take(n * sizeof(float));
+  return L;
+}
+
+BlockCands cands_at(void* ws, const CandLayout& L);
+
 struct DraftLayout {
   BiasGeometry g;
-  size_t pm, ps, cs, ci, ca, bytes;
+  size_t pm, ps, bytes;
+  CandLayout cand;
 };
 
 DraftLayout draft_layout(const dspark_problem* p) {
   DraftLayout L;
-  L.g = bias_geometry(p->R, p->V);
+  L.g = bias_geometry(kModeDraft, p->R, p->V);
   const size_t n = (size_t)p->R * L.g.nsplit;
   Carver c;
   L.pm = c.take(n * sizeof(float));
   L.ps = c.take(n * sizeof(double));
-  L.cs = c.take(n * sizeof(double));
-  L.ci = c.take(n * sizeof(int32_t));
-  L.ca = c.take(n * sizeof(double));
+  L.cand = take_cands(c, n);
   L.bytes = c.off;
   return L;
 }
 
+// Splits per bonus row: about 2048 workgroups in all, whole 32-token blocks.
+int bonus_splits(int R, int V) {
+  const int ntiles = (V + kTile - 1) / kTile;
+  const int ns = (2048 + R - 1) / R;
+  return ns < 1 ? 1 : (ns > ntiles ? ntiles : ns);
+}
+
 struct VerifyLayout {
   BiasGeometry gc, gr;
-  int ns_t, chunk_t, ns_b, chunk_b;
+  int ns_t, chunk_t, ns_b;
   size_t row_ids, counts, req_off, req_len, req_slot, req_mode, resid_ids, bonus_ids;
-  size_t lt_m, lt_s, lse_t, c_s, r_score, r_idx, r_fscore, r_fidx, b_score, b_idx, bytes;
+  size_t lt_m, lt_s, lse_t, c_s, r_wpos, bytes;
+  CandLayout r_cand, r_candf, b_cand;
 };
 
 VerifyLayout verify_layout(const dspark_problem* p) {
   VerifyLayout L;
   const size_t R = p->R, rows = (size_t)p->R * p->gamma;
-  L.gc = bias_geometry((int)rows, p->V);
-  L.gr = bias_geometry(p->R, p->V);
+  L.gc = bias_geometry(kModeCstar, (int)rows, p->V);
+  L.gr = bias_geometry(kModeResidual, p->R, p->V);
   L.ns_t = row_split_count((int)rows, p->V, &L.chunk_t);
-  L.ns_b = row_split_count(p->R, p->V, &L.chunk_b);
+  L.ns_b = bonus_splits(p->R, p->V);
   Carver c;
   L.row_ids = c.take(rows * 4);
   L.counts = c.take(4 * 4);
@@ -112,12 +134,10 @@ VerifyLayout verify_layout(const dspark_problem* p) {
   L.lt_s = c.take(rows * L.ns_t * sizeof(double));
   L.lse_t = c.take(R * (p->gamma + 1) * sizeof(double));
   L.c_s = c.take(rows * L.gc.nsplit * sizeof(double));
-  L.r_score = c.take(R * L.gr.nsplit * sizeof(double));
-  L.r_idx = c.take(R * L.gr.nsplit * sizeof(int32_t));
-  L.r_fscore = c.take(R * L.gr.nsplit * sizeof(double));
-  L.r_fidx = c.take(R * L.gr.nsplit * sizeof(int32_t));
-  L.b_score = c.take(R * L.ns_b * sizeof(double));
-  L.b_idx = c.take(R * L.ns_b * sizeof(int32_t));
+  L.r_cand = take_cands(c, R * L.gr.nsplit);
+  L.r_candf = take_cands(c, R * L.gr.nsplit);
+  L.r_wpos = c.take(R * L.gr.nsplit * sizeof(float));
+  L.b_cand = take_cands(c, R * L.ns_b);
   L.bytes = c.off;
   return L;
 }
@@ -154,6 +174,15 @@ int check_weights(const void* W1, const void* W2p) {
 template <typename T>
 T* at(void* base, size_t off) {
   return reinterpret_cast<T*>(static_cast<char*>(base) + off);
+}
+
+BlockCands cands_at(void* ws, const CandLayout& L) {
+  BlockCands c;
+  c.lo = at<float>(ws, L.lo);
+  c.hi1 = at<float>(ws, L.hi1);
+  c.b1 = at<int32_t>(ws, L.b1);
+  c.hi2 = at<float>(ws, L.hi2);
+  return c;
 }
 
 size_t packed_bytes(const dspark_problem* p) {
@@ -305,20 +334,37 @@ __attribute__((visibility("default"))) int dspark_draft_step(
   a.tokens = tokens;
   a.ntiles = (p->V + kTile - 1) / kTile;
   a.vec_ok = rows_vec_ok(p, U, nullptr);
-  a.tiles_per_split = L.g.tiles_per_split;
+  a.tiles_per_stage = L.g.tiles_per_stage;
   a.nsplit = L.g.nsplit;
   a.pm = at<float>(ws, L.pm);
   a.ps = at<double>(ws, L.ps);
-  a.cscore = at<double>(ws, L.cs);
-  a.cidx = at<int32_t>(ws, L.ci);
-  a.caux = at<double>(ws, L.ca);
+  a.cand = cands_at(ws, L.cand);
+  SelectArgs q = {};
+  q.R = p->R;
+  q.gamma = p->gamma;
+  q.V = p->V;
+  q.seed = p->seed;
+  q.ntiles = a.ntiles;
+  q.nsplit = a.nsplit;
+  q.tiles_per_stage = a.tiles_per_stage;
+  q.U = U;
+  q.W1 = W1;
+  q.W2p = W2p;
+  q.anchors = anchors;
+  q.tokens = tokens;
+  q.pm = a.pm;
+  q.ps = a.ps;
+  q.cand = a.cand;
+  q.out_tokens = tokens;
+  q.out_lse = lse;
+  q.out_logq = logq;
   for (int k = 1; k <= p->gamma; ++k) {
     a.k = k;
+    q.k = k;
     hipError_t e = launch_bias_pass(kModeDraft, bf16, a, s);
     if (e != hipSuccess) return hip_fail(e, "draft pass");
-    e = launch_draft_merge(p->R, p->gamma, k, a.nsplit, a.pm, a.ps, a.cscore, a.cidx, a.caux,
-                           tokens, lse, logq, s);
-    if (e != hipSuccess) return hip_fail(e, "draft merge");
+    e = launch_select(kSelDraft, bf16, q, s);
+    if (e != hipSuccess) return hip_fail(e, "draft select");
   }
   return ok();
 }
@@ -350,18 +396,16 @@ __attribute__((visibility("default"))) int dspark_verify(
   w.lt_s = at<double>(ws, L.lt_s);
   w.lse_t = at<double>(ws, L.lse_t);
   w.c_s = at<double>(ws, L.c_s);
-  w.r_score = at<double>(ws, L.r_score);
-  w.r_idx = at<int32_t>(ws, L.r_idx);
-  w.r_fscore = at<double>(ws, L.r_fscore);
-  w.r_fidx = at<int32_t>(ws, L.r_fidx);
-  w.b_score = at<double>(ws, L.b_score);
-  w.b_idx = at<int32_t>(ws, L.b_idx);
+  w.r_cand = cands_at(ws, L.r_cand);
+  w.r_candf = cands_at(ws, L.r_candf);
+  w.r_wpos = at<float>(ws, L.r_wpos);
+  w.b_cand = cands_at(ws, L.b_cand);
   w.ns_t = L.ns_t;
   w.ns_c = L.gc.nsplit;
   w.ns_r = L.gr.nsplit;
   w.ns_b = L.ns_b;
   w.tps_t = L.chunk_t;
-  w.tps_b = L.chunk_b;
+  w.tps_b = 0;
   w.vec_ok = rows_vec_ok(p, nullptr, T);
 
   hipError_t e = launch_build_rows(p->R, p->gamma, lengths, w, s);
@@ -391,27 +435,58 @@ __attribute__((visibility("default"))) int dspark_verify(
   a.row_ids = w.row_ids;
   a.row_count = w.counts + 0;
   a.nrows = p->R * p->gamma;
-  a.tiles_per_split = L.gc.tiles_per_split;
+  a.tiles_per_stage = L.gc.tiles_per_stage;
   a.nsplit = L.gc.nsplit;
   a.ps = w.c_s;
   e = launch_bias_pass(kModeCstar, bf16, a, s);
   if (e != hipSuccess) return hip_fail(e, "cstar pass");
-  // residual draw at each request's first rejection
+  // residual draw at each request's first rejection: block records ...
   a.row_ids = w.resid_ids;
   a.row_count = w.counts + 1;
   a.nrows = p->R;
-  a.tiles_per_split = L.gr.tiles_per_split;
+  a.tiles_per_stage = L.gr.tiles_per_stage;
   a.nsplit = L.gr.nsplit;
   a.ps = nullptr;
-  a.cscore = w.r_score;
-  a.cidx = w.r_idx;
-  a.fscore = w.r_fscore;
-  a.fidx = w.r_fidx;
+  a.cand = w.r_cand;
+  a.cand_f = w.r_candf;
+  a.wpos = w.r_wpos;
   e = launch_bias_pass(kModeResidual, bf16, a, s);
   if (e != hipSuccess) return hip_fail(e, "residual pass");
+  // ... and the bonus draw's block records
   e = launch_bonus(bf16, p->R, p->gamma, p->V, p->seed, T, w, s);
   if (e != hipSuccess) return hip_fail(e, "bonus pass");
-  e = launch_finalize(p->R, p->gamma, w, cstar, out_token, s);
+  SelectArgs q = {};
+  q.R = p->R;
+  q.gamma = p->gamma;
+  q.V = p->V;
+  q.seed = p->seed;
+  q.ntiles = a.ntiles;
+  q.U = U;
+  q.T = T;
+  q.W1 = W1;
+  q.W2p = W2p;
+  q.anchors = anchors;
+  q.tokens = tokens;
+  q.lse_d = lse_d;
+  q.lse_t = w.lse_t;
+  q.out_tokens = out_token;
+  q.row_ids = w.resid_ids;
+  q.row_count = w.counts + 1;
+  q.nsplit = L.gr.nsplit;
+  q.tiles_per_stage = L.gr.tiles_per_stage;
+  q.cand = w.r_cand;
+  q.cand_f = w.r_candf;
+  q.wpos = w.r_wpos;
+  e = launch_select(kSelResidual, bf16, q, s);
+  if (e != hipSuccess) return hip_fail(e, "residual select");
+  q.row_ids = w.bonus_ids;
+  q.row_count = w.counts + 2;
+  q.nsplit = L.ns_b;
+  q.tiles_per_stage = 1;
+  q.cand = w.b_cand;
+  e = launch_select(kSelBonus, bf16, q, s);
+  if (e != hipSuccess) return hip_fail(e, "bonus select");
+  e = launch_finalize(p->R, p->gamma, w, cstar, s);
   if (e != hipSuccess) return hip_fail(e, "finalize");
   return ok();
 }

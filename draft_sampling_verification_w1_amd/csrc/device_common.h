@@ -19,8 +19,17 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
-// Random-number streams (one per kind of draw).
+// Random-number streams.  A two-level draw takes its block variates from
+// stream s and its member variates from stream s + kMemberStream.
 constexpr uint32_t kStreamDraft = 0, kStreamAccept = 1, kStreamResidual = 2, kStreamBonus = 3;
+constexpr uint32_t kMemberStream = 4;
+
+// Error bounds of the binary32 block scores of the split passes (see
+// BlockCands): |score32 - score64| <= kScoreAbs + kScoreRel * |max logit of
+// the block|, which covers the rounding of the logits, of the 32-term sums,
+// of the hardware exp2/log2 and of the Gumbel transform with a wide margin.
+constexpr float kScoreAbs = 0x1p-12f;
+constexpr float kScoreRel = 0x1p-17f;
 
 // ---------------------------------------------------------------------------
 // Philox4x32-10 (Salmon, Moraes, Dror, Shaw, SC'11): ten rounds of two
@@ -195,6 +204,43 @@ __device__ __forceinline__ T xor32(T v) {
 // Partial records written per (vocabulary split, row) and merged later.
 // Arrays are structure-of-arrays with row stride `ld` (the row capacity).
 // ---------------------------------------------------------------------------
+// Running block-candidate record of a split (see BlockCands).
+struct CandState {
+  float lo, hi1, hi2;
+  int b1;
+  __device__ void init() {
+    lo = hi1 = hi2 = -INFINITY;
+    b1 = -1;
+  }
+  __device__ void add(float lo_b, float hi_b, int b) {
+    lo = fmaxf(lo, lo_b);
+    if (hi_b > hi1) {
+      hi2 = hi1;
+      hi1 = hi_b;
+      b1 = b;
+    } else {
+      hi2 = fmaxf(hi2, hi_b);
+    }
+  }
+  // Merge another split-part's record (disjoint blocks).
+  __device__ void merge(const CandState& o) {
+    lo = fmaxf(lo, o.lo);
+    if (o.hi1 > hi1 || (o.hi1 == hi1 && o.b1 >= 0 && (b1 < 0 || o.b1 < b1))) {
+      hi2 = fmaxf(hi1, o.hi2);
+      hi1 = o.hi1;
+      b1 = o.b1;
+    } else {
+      hi2 = fmaxf(hi2, o.hi1);
+    }
+  }
+  __device__ void store(const BlockCands& c, int64_t o) const {
+    c.lo[o] = lo;
+    c.hi1[o] = hi1;
+    c.b1[o] = b1;
+    c.hi2[o] = hi2;
+  }
+};
+
 struct LsePartials {
   float* m;
   double* s;

@@ -25,6 +25,18 @@ class TimingScope {
   hipStream_t stream_;
 };
 
+// Partial results of a two-level Gumbel-max draw, one record per (row, split).
+// Block b (vocabulary entries [32b, 32b+32)) has a binary32 score whose exact
+// binary64 value lies in [lo_b, hi_b].  The record keeps the split's largest
+// lower bound, its largest upper bound with that block, and the second largest
+// upper bound; a later binary64 pass rescores every block that can still win.
+struct BlockCands {
+  float* lo;
+  float* hi1;
+  int32_t* b1;
+  float* hi2;
+};
+
 // Arguments of one split-vocabulary pass over a set of (request, position)
 // rows: bias B = W1[x_{k-1}] W2 plus backbone logits U, consumed by a
 // mode-specific epilogue.  Partial records are indexed [row * nsplit + split].
@@ -45,32 +57,62 @@ struct BiasPassArgs {
   const double* lse_t;        // [R*(gamma+1)]
   int ntiles;                 // ceil(V / 32)
   int vec_ok;                 // U/T rows 16-byte aligned: vector loads allowed
-  int tiles_per_split;
+  int tiles_per_stage;        // tiles per pipeline stage (split granularity)
   int nsplit;
   float* pm;                  // draft: running max per partial
   double* ps;                 // draft: sum of exp; cstar: sum of min(p^d, p^t)
-  double* cscore;             // candidate partials (draft, residual)
-  int32_t* cidx;
-  double* caux;               // draft: z at the candidate
-  double* fscore;             // residual pass: fallback candidates over ln p^t
-  int32_t* fidx;
+  BlockCands cand;            // draft: blocks of p^d; residual: blocks of max(0, p^t - p^d)
+  BlockCands cand_f;          // residual: blocks of p^t (empty-residual fallback)
+  float* wpos;                // residual: residual mass seen by the split
 };
 
 struct BiasGeometry {
   int rows_per_block;  // 256
   int row_blocks;
-  int tiles_per_split;
+  int tiles_per_stage;
   int nsplit;
 };
-BiasGeometry bias_geometry(int nrows, int V);
+BiasGeometry bias_geometry(int mode, int nrows, int V);
+
+// First tile of split `s` of a pass with `nsplit` splits over ntiles tiles
+// grouped in stages of `tps` tiles (split s covers [split_tile(s), split_tile(s+1))).
+__host__ __device__ inline int split_tile(int s, int nsplit, int ntiles, int tps) {
+  const int nstages = (ntiles + tps - 1) / tps;
+  const int st = (int)((int64_t)s * nstages / nsplit);
+  const int t = st * tps;
+  return t < ntiles ? t : ntiles;
+}
 
 hipError_t launch_bias_pass(int mode, bool bf16, const BiasPassArgs& a, hipStream_t stream);
 
-// Merge draft partials of position k into tokens / lse / logq.
-hipError_t launch_draft_merge(int R, int gamma, int k, int nsplit, const float* pm,
-                              const double* ps, const double* cscore, const int32_t* cidx,
-                              const double* caux, int32_t* tokens, double* lse, double* logq,
-                              hipStream_t stream);
+// Binary64 final stage of a two-level draw: merges the split records of each
+// row, rescores the blocks that can still win and draws the member.
+enum SelectMode { kSelDraft = 0, kSelResidual = 1, kSelBonus = 2 };
+struct SelectArgs {
+  int R, gamma, V;
+  uint64_t seed;
+  int k;                      // draft position (draft mode)
+  int ntiles, nsplit, tiles_per_stage;
+  const int32_t* row_ids;     // residual: r*gamma + (k*-1); bonus: r*(gamma+1) + l_r
+  const int32_t* row_count;   // device count of rows in row_ids
+  const void* U;
+  const void* T;
+  const void* W1;
+  const void* W2p;
+  const int32_t* anchors;
+  const int32_t* tokens;
+  const double* lse_d;        // residual mode
+  const double* lse_t;        // residual mode
+  const float* pm;            // draft: lse partials
+  const double* ps;
+  BlockCands cand;
+  BlockCands cand_f;
+  const float* wpos;
+  int32_t* out_tokens;        // draft: tokens [R, gamma]; residual / bonus: out_token [R]
+  double* out_lse;            // draft
+  double* out_logq;           // draft
+};
+hipError_t launch_select(int mode, bool bf16, const SelectArgs& a, hipStream_t stream);
 
 // ---- verification helpers ------------------------------------------------
 struct VerifyWs {
@@ -86,12 +128,10 @@ struct VerifyWs {
   double* lt_s;
   double* lse_t;        // [R*(gamma+1)] merged, NaN where not computed
   double* c_s;          // [R*gamma*ns_c] c* partial sums
-  double* r_score;      // [R*ns_r] residual candidates
-  int32_t* r_idx;
-  double* r_fscore;
-  int32_t* r_fidx;
-  double* b_score;      // [R*ns_b] bonus candidates
-  int32_t* b_idx;
+  BlockCands r_cand;    // [R*ns_r] residual draw records
+  BlockCands r_candf;   // [R*ns_r] its p^t fallback records
+  float* r_wpos;        // [R*ns_r]
+  BlockCands b_cand;    // [R*ns_b] bonus draw records
   int ns_t, ns_c, ns_r, ns_b;
   int tps_t, tps_b;     // elements per split for the row-streaming passes
   int vec_ok;           // T rows 16-byte aligned: vector loads allowed
@@ -109,8 +149,7 @@ hipError_t launch_decide(bool bf16, int R, int gamma, int V, uint64_t seed, cons
                          hipStream_t stream);
 hipError_t launch_bonus(bool bf16, int R, int gamma, int V, uint64_t seed, const void* T,
                         const VerifyWs& w, hipStream_t stream);
-hipError_t launch_finalize(int R, int gamma, const VerifyWs& w, float* cstar,
-                           int32_t* out_token, hipStream_t stream);
+hipError_t launch_finalize(int R, int gamma, const VerifyWs& w, float* cstar, hipStream_t stream);
 
 // ---- other stages ---------------------------------------------------------
 hipError_t launch_pack_w2(bool bf16, int V, const void* W2, void* W2p, hipStream_t stream);

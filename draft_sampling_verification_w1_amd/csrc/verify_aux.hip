@@ -4,9 +4,9 @@
 //   decide     : acceptance test of each drafted token, first rejection,
 //                residual / bonus work lists (standard speculative rejection
 //                sampling; notes page 배경, summary page 요약)
-//   bonus      : Gumbel-argmax over T[r, l_r] when every verified token is
-//                accepted (bonus token from p^t_{l_r+1})
-//   finalize   : c* per row and the corrective / bonus token per request
+//   bonus      : first level of the two-level Gumbel-max draw over T[r, l_r]
+//                when every verified token is accepted (bonus token from p^t_{l_r+1})
+//   finalize   : c* per (request, position)
 #include "device_common.h"
 #include "kernels.h"
 
@@ -57,34 +57,6 @@ __device__ __forceinline__ void block_lse(float& m, double& s) {
   __syncthreads();
   if (threadIdx.x == 0) {
     for (int w = 1; w < 4; ++w) lse_merge(m, s, sm[w], ss[w]);
-  }
-  __syncthreads();
-}
-
-__device__ __forceinline__ void block_best(double& sc, int& idx) {
-  __shared__ double ssc[4];
-  __shared__ int sidx[4];
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const double s2 = __shfl_xor(sc, off, 64);
-    const int i2 = __shfl_xor(idx, off, 64);
-    if (cand_better(s2, i2, sc, idx)) {
-      sc = s2;
-      idx = i2;
-    }
-  }
-  const int wave = threadIdx.x >> 6;
-  if ((threadIdx.x & 63) == 0) {
-    ssc[wave] = sc;
-    sidx[wave] = idx;
-  }
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    for (int w = 1; w < 4; ++w)
-      if (cand_better(ssc[w], sidx[w], sc, idx)) {
-        sc = ssc[w];
-        idx = sidx[w];
-      }
   }
   __syncthreads();
 }
@@ -226,119 +198,99 @@ __global__ __launch_bounds__(256) void k_decide(int R, int gamma, int V, uint64_
   }
 }
 
+// Bonus draw, first level: per 32-token block of the target row T[r, l_r]
+// (p^t_{l_r+1}), the block log-mass plus its Gumbel variate (stream 3), kept
+// as split records for the binary64 select stage.  A quad of threads covers
+// one block (8 tokens each).
 template <typename E>
 __global__ __launch_bounds__(256) void k_bonus(int gamma, int V, uint64_t seed, const E* T,
                                                VerifyWs w) {
+  __shared__ float slo[4], shi1[4], shi2[4];
+  __shared__ int sb1[4];
   const int i = blockIdx.x;
   if (i >= w.counts[2]) return;
   const int id = w.bonus_ids[i];
   const int r = id / (gamma + 1);
-  const int b = id - r * (gamma + 1) + 1;
+  const int kb = id - r * (gamma + 1) + 1;
   const E* row = T + (int64_t)id * V;
+  const int ntiles = (V + kTile - 1) / kTile;
   const int split = blockIdx.y;
-  const int v0 = split * w.tps_b;
-  const int v1 = min(V, v0 + w.tps_b);
+  const int t0 = split_tile(split, w.ns_b, ntiles, 1);
+  const int t1 = split_tile(split + 1, w.ns_b, ntiles, 1);
   const bool vec_ok = w.vec_ok != 0;
-  float best = -INFINITY, bt = 0.f;
-  int bidx = -1;
-  uint32_t bw = 0;
-  for (int v = v0 + 8 * threadIdx.x; v < v1; v += 8 * 256) {
+  CandState cs;
+  cs.init();
+  for (int v = t0 * kTile + 8 * (int)threadIdx.x; v < t1 * kTile; v += 8 * 256) {
     float x[8];
-    load8(row, v, v1, vec_ok, x);
+    load8(row, v, V, vec_ok, x);
+    float m = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])), fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
+    m = fmaxf(m, __shfl_xor(m, 1, 64));
+    m = fmaxf(m, __shfl_xor(m, 2, 64));
+    float s = 0.f;
+    if (m > -INFINITY) {
+      float e[8];
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      const u32x4 wb = noise_block(seed, kStreamBonus, r, b, (uint32_t)(v >> 2) + q);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int j = 4 * q + e;
-        if (v + j < v1) {
-          const uint32_t wd = word_of(wb, e);
-          const float sc = x[j] + gumbel_f32(wd);
-          if (sc > best) {
-            best = sc;
-            bidx = v + j;
-            bt = x[j];
-            bw = wd;
-          }
-        }
-      }
+      for (int j = 0; j < 8; ++j) e[j] = __builtin_amdgcn_exp2f((x[j] - m) * kLog2e);
+      s = ((e[0] + e[1]) + (e[2] + e[3])) + ((e[4] + e[5]) + (e[6] + e[7]));
+    }
+    s += __shfl_xor(s, 1, 64);
+    s += __shfl_xor(s, 2, 64);
+    if ((threadIdx.x & 3) == 0 && m > -INFINITY) {
+      const int blk = v / kTile;
+      const u32x4 words = noise_block(seed, kStreamBonus, r, kb, (uint32_t)blk >> 2);
+      const float sc = fmaf(__builtin_amdgcn_logf(s), kLn2, m) + gumbel_f32(word_of(words, blk & 3));
+      const float d = fmaf(kScoreRel, fabsf(m), kScoreAbs);
+      cs.add(sc - d, sc + d, blk);
     }
   }
-  double sc = bidx >= 0 ? (double)bt + gumbel_f64(bw) : -INFINITY;
-  block_best(sc, bidx);
-  if (threadIdx.x == 0) {
-    const int64_t o = (int64_t)i * w.ns_b + split;
-    w.b_score[o] = sc;
-    w.b_idx[o] = bidx;
-  }
-}
-
-__device__ __forceinline__ void wave_best(double& sc, int& idx) {
 #pragma unroll
   for (int off = 1; off < 64; off <<= 1) {
-    const double s2 = __shfl_xor(sc, off, 64);
-    const int i2 = __shfl_xor(idx, off, 64);
-    if (cand_better(s2, i2, sc, idx)) {
-      sc = s2;
-      idx = i2;
+    CandState o;
+    o.lo = __shfl_xor(cs.lo, off, 64);
+    o.hi1 = __shfl_xor(cs.hi1, off, 64);
+    o.hi2 = __shfl_xor(cs.hi2, off, 64);
+    o.b1 = __shfl_xor(cs.b1, off, 64);
+    cs.merge(o);
+  }
+  const int wave = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) {
+    slo[wave] = cs.lo;
+    shi1[wave] = cs.hi1;
+    shi2[wave] = cs.hi2;
+    sb1[wave] = cs.b1;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    for (int x = 1; x < 4; ++x) {
+      CandState o;
+      o.lo = slo[x];
+      o.hi1 = shi1[x];
+      o.hi2 = shi2[x];
+      o.b1 = sb1[x];
+      cs.merge(o);
     }
+    cs.store(w.b_cand, (int64_t)i * w.ns_b + split);
   }
 }
 
-// One wave per verified-position entry (c* sum over the vocabulary splits),
-// then one wave per request (corrective or bonus token over its splits).
-__global__ __launch_bounds__(256) void k_finalize(int R, int gamma, VerifyWs w, float* cstar,
-                                                  int32_t* out_token) {
+// One wave per (request, position) entry: c* = sum of its vocabulary splits
+// (NaN beyond the request's verify length).
+__global__ __launch_bounds__(256) void k_finalize(int R, int gamma, VerifyWs w, float* cstar) {
   const int lane = threadIdx.x & 63;
   const int item = blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int n_c = R * gamma;
-  if (item < n_c) {
-    const int r = item / gamma;
-    const int k = item - r * gamma + 1;
-    if (k > w.req_len[r]) {
-      if (lane == 0) cstar[item] = NAN;
-      return;
-    }
-    const int64_t base = (int64_t)(w.req_off[r] + k - 1) * w.ns_c;
-    double s = 0.0;
-    for (int j = lane; j < w.ns_c; j += 64) s += w.c_s[base + j];
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) s += __shfl_xor(s, off, 64);
-    if (lane == 0) cstar[item] = (float)s;
+  if (item >= R * gamma) return;
+  const int r = item / gamma;
+  const int k = item - r * gamma + 1;
+  if (k > w.req_len[r]) {
+    if (lane == 0) cstar[item] = NAN;
     return;
   }
-  const int r = item - n_c;
-  if (r >= R) return;
-  const int slot = w.req_slot[r];
-  double sc = -INFINITY;
-  int idx = -1;
-  if (w.req_mode[r] == 1) {
-    const int64_t base = (int64_t)slot * w.ns_r;
-    for (int j = lane; j < w.ns_r; j += 64)
-      if (cand_better(w.r_score[base + j], w.r_idx[base + j], sc, idx)) {
-        sc = w.r_score[base + j];
-        idx = w.r_idx[base + j];
-      }
-    wave_best(sc, idx);
-    if (idx < 0) {  // empty residual after rounding: draw from p^t instead
-      sc = -INFINITY;
-      for (int j = lane; j < w.ns_r; j += 64)
-        if (cand_better(w.r_fscore[base + j], w.r_fidx[base + j], sc, idx)) {
-          sc = w.r_fscore[base + j];
-          idx = w.r_fidx[base + j];
-        }
-      wave_best(sc, idx);
-    }
-  } else {
-    const int64_t base = (int64_t)slot * w.ns_b;
-    for (int j = lane; j < w.ns_b; j += 64)
-      if (cand_better(w.b_score[base + j], w.b_idx[base + j], sc, idx)) {
-        sc = w.b_score[base + j];
-        idx = w.b_idx[base + j];
-      }
-    wave_best(sc, idx);
-  }
-  if (lane == 0) out_token[r] = idx;
+  const int64_t base = (int64_t)(w.req_off[r] + k - 1) * w.ns_c;
+  double s = 0.0;
+  for (int j = lane; j < w.ns_c; j += 64) s += w.c_s[base + j];
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) s += __shfl_xor(s, off, 64);
+  if (lane == 0) cstar[item] = (float)s;
 }
 
 }  // namespace
@@ -399,12 +351,10 @@ hipError_t launch_bonus(bool bf16, int R, int gamma, int V, uint64_t seed, const
   return hipGetLastError();
 }
 
-hipError_t launch_finalize(int R, int gamma, const VerifyWs& w, float* cstar, int32_t* out_token,
-                           hipStream_t stream) {
+hipError_t launch_finalize(int R, int gamma, const VerifyWs& w, float* cstar, hipStream_t stream) {
   TimingScope timing("finalize", stream);
-  const int waves = R * gamma + R;
-  hipLaunchKernelGGL(k_finalize, dim3((waves + 3) / 4), dim3(256), 0, stream, R, gamma, w, cstar,
-                     out_token);
+  const int waves = R * gamma;
+  hipLaunchKernelGGL(k_finalize, dim3((waves + 3) / 4), dim3(256), 0, stream, R, gamma, w, cstar);
   return hipGetLastError();
 }
 
