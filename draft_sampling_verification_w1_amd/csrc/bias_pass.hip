@@ -36,6 +36,11 @@ constexpr int kTileBytesA = kSteps * 64 * 16;  // one packed W2 tile (16 KB)
 
 typedef __attribute__((address_space(3))) uint8_t lds_u8;
 
+// Eight bf16 -inf: the staging source of row segments beyond V and of rows
+// that are not active, so the epilogues need no masks.
+__device__ __attribute__((aligned(16))) const uint32_t kNegInfBf16x8[4] = {0xFF80FF80u, 0xFF80FF80u,
+                                                                            0xFF80FF80u, 0xFF80FF80u};
+
 // 16 bytes per lane, global -> LDS; lane i lands at `lds` + 16 i (`lds` is
 // wave-uniform).  Issued as inline assembly so that the compiler does not
 // order later LDS reads of other ring buffers behind these copies: their
@@ -87,8 +92,8 @@ struct RowCtx {
   int prev;
   const void* urow;
   const void* trow;
-  float ld32, lt32;
-  float eps;  // residual: relative error bound of the binary32 p^d, p^t
+  float ld2, lt2;  // log2(e) * lse of p^d and p^t
+  float eps;       // residual: relative error bound of the binary32 p^d, p^t
 };
 
 __device__ __forceinline__ RowCtx row_ctx(const BiasPassArgs& a, int i, int active_rows, bool bf16) {
@@ -99,7 +104,7 @@ __device__ __forceinline__ RowCtx row_ctx(const BiasPassArgs& a, int i, int acti
   c.prev = 0;
   c.urow = nullptr;
   c.trow = nullptr;
-  c.ld32 = c.lt32 = 0.f;
+  c.ld2 = c.lt2 = 0.f;
   c.eps = 0.f;
   if (!c.active) return c;
   if (a.row_ids) {
@@ -115,9 +120,12 @@ __device__ __forceinline__ RowCtx row_ctx(const BiasPassArgs& a, int i, int acti
   const size_t esz = bf16 ? 2 : 4;
   c.urow = (const char*)a.U + ((int64_t)c.r * a.gamma + (c.k - 1)) * (int64_t)a.V * esz;
   if (a.T) c.trow = (const char*)a.T + ((int64_t)c.r * (a.gamma + 1) + (c.k - 1)) * (int64_t)a.V * esz;
-  if (a.lse_d) c.ld32 = (float)a.lse_d[(int64_t)c.r * a.gamma + (c.k - 1)];
-  if (a.lse_t) c.lt32 = (float)a.lse_t[(int64_t)c.r * (a.gamma + 1) + (c.k - 1)];
-  c.eps = 0x1p-15f + 0x1p-21f * (fabsf(c.ld32) + fabsf(c.lt32));
+  float ld = 0.f, lt = 0.f;
+  if (a.lse_d) ld = (float)a.lse_d[(int64_t)c.r * a.gamma + (c.k - 1)];
+  if (a.lse_t) lt = (float)a.lse_t[(int64_t)c.r * (a.gamma + 1) + (c.k - 1)];
+  c.ld2 = ld * kLog2e;
+  c.lt2 = lt * kLog2e;
+  c.eps = 0x1p-15f + 0x1p-21f * (fabsf(ld) + fabsf(lt));
   return c;
 }
 
@@ -195,24 +203,22 @@ struct LaneState<kModeResidual> {
   }
 };
 
-// Per-tile epilogue: the lane holds the bias acc[j] of tokens vb + j (j < 16)
-// of one row (block t = its tile), with that row's backbone logits u[j] (and
-// target logits tv[j]); entries at or beyond V hold -inf in u and tv.
+// Per-tile epilogue: the lane holds the draft logits z[j] = U + B of tokens
+// vb + j (j < 16) of one row (block t = its tile) and, in the verify modes, the
+// target logits tv[j]; entries at or beyond V hold -inf.  Exponentials are
+// taken in base 2 with the scaling folded into one fma.
 template <int MODE>
-__device__ __forceinline__ void epilogue(LaneState<MODE>& st, const float* acc, const float* u,
-                                         const float* tv, const RowCtx& rc, int t, bool first,
-                                         uint64_t seed) {
+__device__ __forceinline__ void epilogue(LaneState<MODE>& st, const float* z, const float* tv,
+                                         const RowCtx& rc, int t, bool first, uint64_t seed) {
   if constexpr (MODE == kModeDraft) {
-    float z[16];
-#pragma unroll
-    for (int j = 0; j < 16; ++j) z[j] = u[j] + acc[j];
     if (first || (t & 3) == 0) st.words = noise_block(seed, kStreamDraft, rc.r, rc.k, (uint32_t)t >> 2);
     const float ml = max16(z);
     const float mt = fmaxf(ml, xor32(ml));
     if (mt == -INFINITY) return;  // block without mass
+    const float mt2 = mt * kLog2e;
     float e[16];
 #pragma unroll
-    for (int j = 0; j < 16; ++j) e[j] = __builtin_amdgcn_exp2f((z[j] - mt) * kLog2e);
+    for (int j = 0; j < 16; ++j) e[j] = __builtin_amdgcn_exp2f(fmaf(z[j], kLog2e, -mt2));
     const float sl = sum16(e);
     const float s = sl + xor32(sl);
     if (mt > st.M) {
@@ -227,18 +233,15 @@ __device__ __forceinline__ void epilogue(LaneState<MODE>& st, const float* acc, 
   } else if constexpr (MODE == kModeCstar) {
     float e[16];
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const float lpd = (u[j] - rc.ld32) + acc[j];
-      const float lpt = tv[j] - rc.lt32;
-      e[j] = __builtin_amdgcn_exp2f(fminf(lpd, lpt) * kLog2e);
-    }
+    for (int j = 0; j < 16; ++j)
+      e[j] = __builtin_amdgcn_exp2f(fminf(fmaf(z[j], kLog2e, -rc.ld2), fmaf(tv[j], kLog2e, -rc.lt2)));
     st.s += (double)sum16(e);
   } else {
     float w = 0.f, p = 0.f, q = 0.f;
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
-      const float pd = __builtin_amdgcn_exp2f(((u[j] - rc.ld32) + acc[j]) * kLog2e);
-      const float pt = __builtin_amdgcn_exp2f((tv[j] - rc.lt32) * kLog2e);
+      const float pd = __builtin_amdgcn_exp2f(fmaf(z[j], kLog2e, -rc.ld2));
+      const float pt = __builtin_amdgcn_exp2f(fmaf(tv[j], kLog2e, -rc.lt2));
       w += fmaxf(pt - pd, 0.f);
       p += pt + pd;
       q += pt;
@@ -305,7 +308,7 @@ __global__ __launch_bounds__(kThreads) void k_bias_bf16(const BiasPassArgs a) {
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 31;
   const int h = lane >> 5;
   const int active_rows = a.row_count ? min(*a.row_count, a.nrows) : a.nrows;
@@ -332,23 +335,25 @@ __global__ __launch_bounds__(kThreads) void k_bias_bf16(const BiasPassArgs a) {
 
   // Loader: instruction j of this wave fills slots [64 j, 64 j + 64) of the
   // wave's 32-row region; slot p holds row p / NSEG, segment
-  // (p % NSEG) ^ seg_swz(row).
+  // (p % NSEG) ^ seg_swz(row).  ld_u / ld_t: this lane's source address in
+  // stage 0 (null for a row that is not active), advanced by SEG per stage.
   const uint16_t* urow = rc.active ? reinterpret_cast<const uint16_t*>(rc.urow) : nullptr;
   const uint16_t* trow = (rc.active && kNeedT) ? reinterpret_cast<const uint16_t*>(rc.trow) : nullptr;
-  const uint16_t* ld_u[2 * ST];
-  const uint16_t* ld_t[2 * ST];
-  int ld_seg[2 * ST];
+  const uint8_t* ld_u[2 * ST];
+  const uint8_t* ld_t[2 * ST];
+  int ld_tok[2 * ST];  // first token of the lane's segment within a stage
 #pragma unroll
   for (int j = 0; j < 2 * ST; ++j) {
     const int p = 64 * j + lane;
     const int nn = p / NSEG;
-    ld_seg[j] = (p % NSEG) ^ seg_swz<NSEG>(nn);
-    ld_u[j] = reinterpret_cast<const uint16_t*>(__shfl((unsigned long long)(uintptr_t)urow, nn, 64));
-    ld_t[j] = reinterpret_cast<const uint16_t*>(__shfl((unsigned long long)(uintptr_t)trow, nn, 64));
+    ld_tok[j] = ((p % NSEG) ^ seg_swz<NSEG>(nn)) * 8;
+    const uint16_t* ru = reinterpret_cast<const uint16_t*>(__shfl((unsigned long long)(uintptr_t)urow, nn, 64));
+    const uint16_t* rt = reinterpret_cast<const uint16_t*>(__shfl((unsigned long long)(uintptr_t)trow, nn, 64));
+    ld_u[j] = ru ? reinterpret_cast<const uint8_t*>(ru + ld_tok[j]) : nullptr;
+    ld_t[j] = rt ? reinterpret_cast<const uint8_t*>(rt + ld_tok[j]) : nullptr;
   }
-  const uint8_t* W2b = reinterpret_cast<const uint8_t*>(a.W2p);
-  const uint16_t* Ubase = reinterpret_cast<const uint16_t*>(a.U);
-  const uint16_t* Tbase = reinterpret_cast<const uint16_t*>(a.T);
+  const uint8_t* W2lane = reinterpret_cast<const uint8_t*>(a.W2p) + lane * 16;
+  const uint8_t* neg = reinterpret_cast<const uint8_t*>(kNegInfBf16x8);
   // asynchronous loads per wave per stage
   constexpr int lps = 2 * ST * (1 + (VEC ? (kNeedT ? 2 : 1) : 0));
 
@@ -359,24 +364,27 @@ __global__ __launch_bounds__(kThreads) void k_bias_bf16(const BiasPassArgs a) {
     for (int j = 0; j < 2 * ST; ++j) {
       const int q = wave * 2 * ST + j;
       const int tt = min(t0 + q / 16, a.ntiles - 1);
-      dma16(W2b + (int64_t)tt * kTileBytesA + (q % 16) * 1024 + lane * 16, &sA[b][q * 1024]);
+      dma16(W2lane + (int64_t)tt * kTileBytesA + (q % 16) * 1024, &sA[b][q * 1024]);
     }
+    const int v0 = t0 * kTile;
+    const bool full = v0 + ST * kTile <= a.V;  // every segment of the stage inside the row
+    const int64_t off = (int64_t)v0 * 2;
 #pragma unroll
     for (int j = 0; j < 2 * ST; ++j) {
-      const int v = t0 * kTile + ld_seg[j] * 8;
       uint8_t* du = &sU[b][wave * 32 * SEG + j * 1024];
+      uint8_t* dt = &sT[kNeedT ? b : 0][kNeedT ? wave * 32 * SEG + j * 1024 : 0];
       if constexpr (VEC) {
-        const uint16_t* su = ld_u[j] ? (v + 8 <= a.V ? ld_u[j] + v : ld_u[j]) : Ubase;
-        dma16(su, du);
-        if constexpr (kNeedT) {
-          const uint16_t* stp = ld_t[j] ? (v + 8 <= a.V ? ld_t[j] + v : ld_t[j]) : Tbase;
-          dma16(stp, &sT[b][wave * 32 * SEG + j * 1024]);
-        }
+        const bool in = full || v0 + ld_tok[j] + 8 <= a.V;
+        dma16(ld_u[j] && in ? ld_u[j] + off : neg, du);
+        if constexpr (kNeedT) dma16(ld_t[j] && in ? ld_t[j] + off : neg, dt);
       } else {
-        *reinterpret_cast<u32x4*>(du + lane * 16) = chunk_load(ld_u[j], v, a.V);
-        if constexpr (kNeedT)
-          *reinterpret_cast<u32x4*>(&sT[b][wave * 32 * SEG + j * 1024] + lane * 16) =
-              chunk_load(ld_t[j], v, a.V);
+        const int v = v0 + ld_tok[j];
+        const uint16_t* ru = ld_u[j] ? reinterpret_cast<const uint16_t*>(ld_u[j]) - ld_tok[j] : nullptr;
+        *reinterpret_cast<u32x4*>(du + lane * 16) = chunk_load(ru, v, a.V);
+        if constexpr (kNeedT) {
+          const uint16_t* rt = ld_t[j] ? reinterpret_cast<const uint16_t*>(ld_t[j]) - ld_tok[j] : nullptr;
+          *reinterpret_cast<u32x4*>(dt + lane * 16) = chunk_load(rt, v, a.V);
+        }
       }
     }
   };
@@ -385,6 +393,7 @@ __global__ __launch_bounds__(kThreads) void k_bias_bf16(const BiasPassArgs a) {
   for (int pre = 0; pre < NS - 1; ++pre)
     if (c_begin + pre < c_end) issue(c_begin + pre);
 
+  const int sw = seg_swz<NSEG>(n);
   for (int c = c_begin; c < c_end; ++c) {
     // stage c is complete once at most the later stages' loads are in flight
     wait_vmcnt(min(NS - 2, c_end - 1 - c) * lps);
@@ -395,40 +404,28 @@ __global__ __launch_bounds__(kThreads) void k_bias_bf16(const BiasPassArgs a) {
     for (int tau = 0; tau < ST; ++tau) {
       const int t = c * ST + tau;
       if (t >= t_end) break;
-      const u32x4* At = reinterpret_cast<const u32x4*>(&sA[b][tau * kTileBytesA]) + lane;
-      u32x4 av[kSteps];
+      // backbone logits seed the accumulator: the MFMA chain yields z = U + B
+      const int s0 = 4 * tau + 2 * h;
+      const uint8_t* ru = &sU[b][(wave * 32 + n) * SEG];
+      float z[16];
+      decode16(*reinterpret_cast<const u32x4*>(ru + ((s0 ^ sw) * 16)),
+               *reinterpret_cast<const u32x4*>(ru + (((s0 + 1) ^ sw) * 16)), z);
+      f32x16 acc;
 #pragma unroll
-      for (int s = 0; s < kSteps; ++s) av[s] = At[s * 64];
-      f32x16 acc = {};
+      for (int j = 0; j < 16; ++j) acc[j] = z[j];
+      const u32x4* At = reinterpret_cast<const u32x4*>(&sA[b][tau * kTileBytesA]) + lane;
 #pragma unroll
       for (int s = 0; s < kSteps; ++s)
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(av[s]), bop[s], acc, 0, 0, 0);
-      if (rc.active) {
-        float accv[16], u[16], tv[16];
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(At[s * 64]), bop[s], acc, 0, 0, 0);
 #pragma unroll
-        for (int j = 0; j < 16; ++j) accv[j] = acc[j];
-        const int s0 = 4 * tau + 2 * h;
-        const int sw = seg_swz<NSEG>(n);
-        const uint8_t* ru = &sU[b][(wave * 32 + n) * SEG];
-        decode16(*reinterpret_cast<const u32x4*>(ru + ((s0 ^ sw) * 16)),
-                 *reinterpret_cast<const u32x4*>(ru + (((s0 + 1) ^ sw) * 16)), u);
-        if constexpr (kNeedT) {
-          const uint8_t* rt = &sT[b][(wave * 32 + n) * SEG];
-          decode16(*reinterpret_cast<const u32x4*>(rt + ((s0 ^ sw) * 16)),
-                   *reinterpret_cast<const u32x4*>(rt + (((s0 + 1) ^ sw) * 16)), tv);
-        }
-        if (t * kTile + kTile > a.V) {  // ragged last tile
-          const int vb = t * kTile + 16 * h;
-#pragma unroll
-          for (int j = 0; j < 16; ++j) {
-            if (vb + j >= a.V) {
-              u[j] = -INFINITY;
-              tv[j] = -INFINITY;
-            }
-          }
-        }
-        epilogue<MODE>(st, accv, u, tv, rc, t, t == t_begin, a.seed);
+      for (int j = 0; j < 16; ++j) z[j] = acc[j];
+      float tv[16];
+      if constexpr (kNeedT) {
+        const uint8_t* rt = &sT[b][(wave * 32 + n) * SEG];
+        decode16(*reinterpret_cast<const u32x4*>(rt + ((s0 ^ sw) * 16)),
+                 *reinterpret_cast<const u32x4*>(rt + (((s0 + 1) ^ sw) * 16)), tv);
       }
+      epilogue<MODE>(st, z, tv, rc, t, t == t_begin, a.seed);
     }
   }
   finish<MODE>(st, rc, row, split, a, h == 0);
@@ -477,13 +474,13 @@ __global__ __launch_bounds__(kThreads) void k_bias_f32(const BiasPassArgs a) {
           acc[j] = fmaf(x.w, y.w, acc[j]);
         }
       }
-      float u[16], tv[16];
+      float z[16], tv[16];
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
-        u[j] = (vb + j < a.V) ? ur[vb + j] : -INFINITY;
+        z[j] = (vb + j < a.V) ? ur[vb + j] + acc[j] : -INFINITY;
         tv[j] = (kNeedT && vb + j < a.V) ? tr[vb + j] : -INFINITY;
       }
-      epilogue<MODE>(st, acc, u, tv, rc, t, t == t_begin, a.seed);
+      epilogue<MODE>(st, z, tv, rc, t, t == t_begin, a.seed);
     }
   }
   finish<MODE>(st, rc, row, split, a, h == 0);
