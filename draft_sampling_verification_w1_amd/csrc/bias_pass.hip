@@ -11,16 +11,17 @@
 //              (standard speculative rejection sampling, notes page 배경)
 //
 // bf16 rows use the gfx950 matrix cores.  A workgroup owns 256 rows (8 waves x
-// 32 rows) and a contiguous range of 32-token tiles.  Tiles flow through an LDS
-// ring in stages: the packed W2 tiles of a stage (the MFMA A operand, shared by
-// all 8 waves) and the stage's U (and T) row segments are copied global -> LDS
-// with global_load_lds_dwordx4 ahead of use, so no VGPR holds in-flight data
-// and each W2 byte crosses L2 -> CU once per workgroup.  Row segments are
-// placed with an xor swizzle so that the lanes' 16-byte fragment reads hit
-// distinct LDS banks.  The gathered W1 rows of a wave's 32 rows are the B
-// operand, held in registers for the whole pass; v_mfma_f32_32x32x16_bf16
-// accumulates in fp32.  The packed tile order makes lane (n, h) own tokens
-// [16h, 16h+16) of row n, so a 32-token block is the lane pair (n, n+32).
+// 32 rows) and a contiguous range of 32-token tiles, taken two tiles (64
+// tokens) per pipeline stage.  Each wave prefetches several stages ahead into
+// registers and writes a stage to LDS just before it is used: the packed W2
+// tiles (the MFMA A operand, shared by all 8 waves, so each W2 byte crosses
+// L2 -> CU once per workgroup) and 128-byte segments of the wave's own rows of
+// U (and T), placed with an xor swizzle so that the lanes' 16-byte fragment
+// reads hit distinct LDS banks.  The gathered W1 rows of a wave's 32 rows are
+// the B operand, held in registers for the whole pass; v_mfma_f32_32x32x16_bf16
+// accumulates in fp32 on top of the backbone logits.  The packed tile order
+// makes lane (n, h) own tokens [16h, 16h+16) of row n, so a 32-token block is
+// the lane pair (n, n+32).
 // Binary32 rows compute the same bias with a VALU dot product.
 #include "device_common.h"
 #include "kernels.h"
@@ -34,44 +35,8 @@ constexpr int kRowsPerBlock = kWaves * 32;
 constexpr int kThreads = kWaves * 64;
 constexpr int kTileBytesA = kSteps * 64 * 16;  // one packed W2 tile (16 KB)
 
-typedef __attribute__((address_space(3))) uint8_t lds_u8;
-
-// Eight bf16 -inf: the staging source of row segments beyond V and of rows
-// that are not active, so the epilogues need no masks.
-__device__ __attribute__((aligned(16))) const uint32_t kNegInfBf16x8[4] = {0xFF80FF80u, 0xFF80FF80u,
-                                                                            0xFF80FF80u, 0xFF80FF80u};
-
-// 16 bytes per lane, global -> LDS; lane i lands at `lds` + 16 i (`lds` is
-// wave-uniform).  Issued as inline assembly so that the compiler does not
-// order later LDS reads of other ring buffers behind these copies: their
-// completion is tracked explicitly with wait_vmcnt.  M0 is set right before
-// the copy and holds no compiler value here.
-__device__ __forceinline__ void dma16(const void* g, void* lds) {
-  const uint32_t l = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_u8*)lds);
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(l) : "memory");
-}
-
-// s_waitcnt immediate for "at most n vector-memory loads outstanding" (gfx9
-// encoding: vmcnt in bits [3:0] and [15:14]; expcnt and lgkmcnt left free).
-constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | 0x0F70; }
-
-// Wait until at most n of this wave's vector-memory loads are outstanding.
-// Written as the builtin so that the compiler's own wait tracking sees it.
-__device__ __forceinline__ void wait_vmcnt(int n) {
-  switch (n) {
-    case 2: __builtin_amdgcn_s_waitcnt(vmcnt_imm(2)); break;
-    case 4: __builtin_amdgcn_s_waitcnt(vmcnt_imm(4)); break;
-    case 6: __builtin_amdgcn_s_waitcnt(vmcnt_imm(6)); break;
-    case 8: __builtin_amdgcn_s_waitcnt(vmcnt_imm(8)); break;
-    case 12: __builtin_amdgcn_s_waitcnt(vmcnt_imm(12)); break;
-    default: __builtin_amdgcn_s_waitcnt(vmcnt_imm(0)); break;
-  }
-  asm volatile("" ::: "memory");
-}
-
-// Workgroup barrier for the LDS ring.  The caller has already waited for its
-// own loads of the stage (vmcnt); LDS stores must be complete too.  A plain
-// s_barrier: __syncthreads' release fence would also wait for the loads of
+// Workgroup barrier of the stage loop: LDS stores complete, then s_barrier.
+// __syncthreads' release fence would also wait for the register prefetches of
 // later stages that are still in flight.
 __device__ __forceinline__ void stage_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
@@ -141,6 +106,19 @@ __device__ __forceinline__ u32x4 chunk_load(const uint16_t* row, int v, int V) {
     w[i] = lo | (hi << 16);
   }
   return (u32x4){w[0], w[1], w[2], w[3]};
+}
+
+// Eight bf16 -inf: the load source of row segments beyond V and of rows that
+// are not active, so that the loaded value needs no select.
+__device__ __attribute__((aligned(16))) const uint32_t kNegInfBf16x8[4] = {0xFF80FF80u, 0xFF80FF80u,
+                                                                            0xFF80FF80u, 0xFF80FF80u};
+
+typedef __attribute__((address_space(1))) const u32x4 global_u32x4;
+
+// 16-byte load through a global-address-space pointer (a pointer that went
+// through a lane shuffle is otherwise a flat access).
+__device__ __forceinline__ u32x4 gload16(const void* p) {
+  return *(global_u32x4*)(p);
 }
 
 __device__ __forceinline__ void decode16(u32x4 a, u32x4 b, float* out) {
@@ -293,18 +271,23 @@ __device__ __forceinline__ void finish(const LaneState<MODE>& st, const RowCtx& 
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
-// ST tiles per stage, NS stages in the LDS ring; VEC: rows 16-byte aligned
-// (asynchronous global -> LDS copies of U / T), else scalar loads.
-template <int MODE, int ST, int NS, bool VEC>
+// One pipeline stage = 2 tiles (64 tokens).  Every wave prefetches D stages
+// ahead into registers: its 1/8 share of the stage's packed W2 tiles (4 x 16 B
+// per lane) and the 128-byte segments of its own 32 rows of U (and T), 8 rows
+// x 128 B per load instruction.  At its turn a stage is written to LDS: the W2
+// tiles to a double-buffered workgroup area, the row segments to the wave's
+// own area (xor-swizzled 16-byte slots); one barrier per stage publishes the
+// W2 tiles.  VEC: rows 16-byte aligned (vector loads), else scalar loads.
+template <int MODE, int D, bool VEC>
 __global__ __launch_bounds__(kThreads) void k_bias_bf16(const BiasPassArgs a) {
   constexpr bool kNeedT = MODE != kModeDraft;
+  constexpr int ST = 2;
   constexpr int SEG = ST * 64;     // bytes of one row per stage
   constexpr int NSEG = SEG / 16;   // 16-byte segments of one row per stage
   constexpr int kABytes = ST * kTileBytesA;
-  constexpr int kRBytes = kRowsPerBlock * SEG;
-  __shared__ __attribute__((aligned(16))) uint8_t sA[NS][kABytes];
-  __shared__ __attribute__((aligned(16))) uint8_t sU[NS][kRBytes];
-  __shared__ __attribute__((aligned(16))) uint8_t sT[kNeedT ? NS : 1][kNeedT ? kRBytes : 16];
+  constexpr int NR = kNeedT ? 2 : 1;
+  __shared__ __attribute__((aligned(16))) uint8_t sA[2][kABytes];
+  __shared__ __attribute__((aligned(16))) uint8_t sR[kWaves][NR][32 * SEG];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -322,6 +305,71 @@ __global__ __launch_bounds__(kThreads) void k_bias_bf16(const BiasPassArgs a) {
 
   const int row = row0 + wave * 32 + n;
   const RowCtx rc = row_ctx(a, row, active_rows, true);
+  LaneState<MODE> st;
+  st.init();
+
+  // Row loads: instruction i covers rows 8i .. 8i+7 of the wave; lane -> row
+  // 8i + lane/8, segment lane%8 of the stage's 128 bytes.
+  const uint16_t* urow = rc.active ? reinterpret_cast<const uint16_t*>(rc.urow) : nullptr;
+  const uint16_t* trow = (rc.active && kNeedT) ? reinterpret_cast<const uint16_t*>(rc.trow) : nullptr;
+  const int lseg = lane & 7;
+  const uint16_t* ld_u[4];
+  const uint16_t* ld_t[4];
+  int ld_slot[4];  // LDS byte offset of the lane's segment in the wave's area
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int nn = 8 * i + (lane >> 3);
+    ld_u[i] = reinterpret_cast<const uint16_t*>(__shfl((unsigned long long)(uintptr_t)urow, nn, 64));
+    ld_t[i] = reinterpret_cast<const uint16_t*>(__shfl((unsigned long long)(uintptr_t)trow, nn, 64));
+    ld_slot[i] = (nn * NSEG + (lseg ^ seg_swz<NSEG>(nn))) * 16;
+  }
+  const u32x4* W2q = reinterpret_cast<const u32x4*>(a.W2p);
+
+  // Stages c >= c_end are padding (the loop runs whole groups of D stages so
+  // that every stage issues the same loads): their loads read one cached
+  // 16-byte line and nothing they bring is used.
+  u32x4 ra[D][4], ru[D][4], rt[D][kNeedT ? 4 : 1];
+  auto row_seg = [&](const uint16_t* r, int v, bool live) -> u32x4 {
+    if constexpr (VEC) {
+      const bool in = live && r != nullptr && v + 8 <= a.V;
+      return gload16(in ? static_cast<const void*>(r + v) : static_cast<const void*>(kNegInfBf16x8));
+    } else {
+      return live ? chunk_load(r, v, a.V) : gload16(kNegInfBf16x8);
+    }
+  };
+  auto load_stage = [&](int d, int c) {
+    const bool live = c < c_end;
+    const int t0 = c * ST;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int q = wave * 256 + i * 64 + lane;  // 16-byte chunk of the stage's W2 tiles
+      const int tt = min(t0 + (q >> 10), a.ntiles - 1);
+      ra[d][i] = gload16(live ? static_cast<const void*>(W2q + (int64_t)tt * 1024 + (q & 1023))
+                              : static_cast<const void*>(kNegInfBf16x8));
+    }
+    const int v = t0 * kTile + lseg * 8;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      ru[d][i] = row_seg(ld_u[i], v, live);
+      if constexpr (kNeedT) rt[d][i] = row_seg(ld_t[i], v, live);
+    }
+  };
+  auto store_stage = [&](int d, int c) {
+    uint8_t* da = sA[c & 1];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      *reinterpret_cast<u32x4*>(da + (wave * 256 + i * 64 + lane) * 16) = ra[d][i];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      *reinterpret_cast<u32x4*>(&sR[wave][0][ld_slot[i]]) = ru[d][i];
+      if constexpr (kNeedT) *reinterpret_cast<u32x4*>(&sR[wave][NR - 1][ld_slot[i]]) = rt[d][i];
+    }
+  };
+
+#pragma unroll
+  for (int d = 0; d < D; ++d) load_stage(d, c_begin + d);
+  // the W1 gather waits on the previous token; it is issued after the first
+  // stages' loads so that their latency overlaps that chain
   bf16x8 bop[kSteps];
   {
     const u32x4* w1 = reinterpret_cast<const u32x4*>(
@@ -329,103 +377,46 @@ __global__ __launch_bounds__(kThreads) void k_bias_bf16(const BiasPassArgs a) {
 #pragma unroll
     for (int s = 0; s < kSteps; ++s) bop[s] = as_bf16x8(rc.active ? w1[s] : (u32x4){0u, 0u, 0u, 0u});
   }
-  LaneState<MODE> st;
-  st.init();
-  wait_vmcnt(0);  // operands in registers before the ring starts
-
-  // Loader: instruction j of this wave fills slots [64 j, 64 j + 64) of the
-  // wave's 32-row region; slot p holds row p / NSEG, segment
-  // (p % NSEG) ^ seg_swz(row).  ld_u / ld_t: this lane's source address in
-  // stage 0 (null for a row that is not active), advanced by SEG per stage.
-  const uint16_t* urow = rc.active ? reinterpret_cast<const uint16_t*>(rc.urow) : nullptr;
-  const uint16_t* trow = (rc.active && kNeedT) ? reinterpret_cast<const uint16_t*>(rc.trow) : nullptr;
-  const uint8_t* ld_u[2 * ST];
-  const uint8_t* ld_t[2 * ST];
-  int ld_tok[2 * ST];  // first token of the lane's segment within a stage
-#pragma unroll
-  for (int j = 0; j < 2 * ST; ++j) {
-    const int p = 64 * j + lane;
-    const int nn = p / NSEG;
-    ld_tok[j] = ((p % NSEG) ^ seg_swz<NSEG>(nn)) * 8;
-    const uint16_t* ru = reinterpret_cast<const uint16_t*>(__shfl((unsigned long long)(uintptr_t)urow, nn, 64));
-    const uint16_t* rt = reinterpret_cast<const uint16_t*>(__shfl((unsigned long long)(uintptr_t)trow, nn, 64));
-    ld_u[j] = ru ? reinterpret_cast<const uint8_t*>(ru + ld_tok[j]) : nullptr;
-    ld_t[j] = rt ? reinterpret_cast<const uint8_t*>(rt + ld_tok[j]) : nullptr;
-  }
-  const uint8_t* W2lane = reinterpret_cast<const uint8_t*>(a.W2p) + lane * 16;
-  const uint8_t* neg = reinterpret_cast<const uint8_t*>(kNegInfBf16x8);
-  // asynchronous loads per wave per stage
-  constexpr int lps = 2 * ST * (1 + (VEC ? (kNeedT ? 2 : 1) : 0));
-
-  auto issue = [&](int c) {
-    const int b = c % NS;
-    const int t0 = c * ST;
-#pragma unroll
-    for (int j = 0; j < 2 * ST; ++j) {
-      const int q = wave * 2 * ST + j;
-      const int tt = min(t0 + q / 16, a.ntiles - 1);
-      dma16(W2lane + (int64_t)tt * kTileBytesA + (q % 16) * 1024, &sA[b][q * 1024]);
-    }
-    const int v0 = t0 * kTile;
-    const bool full = v0 + ST * kTile <= a.V;  // every segment of the stage inside the row
-    const int64_t off = (int64_t)v0 * 2;
-#pragma unroll
-    for (int j = 0; j < 2 * ST; ++j) {
-      uint8_t* du = &sU[b][wave * 32 * SEG + j * 1024];
-      uint8_t* dt = &sT[kNeedT ? b : 0][kNeedT ? wave * 32 * SEG + j * 1024 : 0];
-      if constexpr (VEC) {
-        const bool in = full || v0 + ld_tok[j] + 8 <= a.V;
-        dma16(ld_u[j] && in ? ld_u[j] + off : neg, du);
-        if constexpr (kNeedT) dma16(ld_t[j] && in ? ld_t[j] + off : neg, dt);
-      } else {
-        const int v = v0 + ld_tok[j];
-        const uint16_t* ru = ld_u[j] ? reinterpret_cast<const uint16_t*>(ld_u[j]) - ld_tok[j] : nullptr;
-        *reinterpret_cast<u32x4*>(du + lane * 16) = chunk_load(ru, v, a.V);
-        if constexpr (kNeedT) {
-          const uint16_t* rt = ld_t[j] ? reinterpret_cast<const uint16_t*>(ld_t[j]) - ld_tok[j] : nullptr;
-          *reinterpret_cast<u32x4*>(dt + lane * 16) = chunk_load(rt, v, a.V);
-        }
-      }
-    }
-  };
-
-#pragma unroll
-  for (int pre = 0; pre < NS - 1; ++pre)
-    if (c_begin + pre < c_end) issue(c_begin + pre);
 
   const int sw = seg_swz<NSEG>(n);
-  for (int c = c_begin; c < c_end; ++c) {
-    // stage c is complete once at most the later stages' loads are in flight
-    wait_vmcnt(min(NS - 2, c_end - 1 - c) * lps);
-    stage_barrier();  // stage c visible to every wave; stage c-1 fully consumed
-    if (c + NS - 1 < c_end) issue(c + NS - 1);
-    const int b = c % NS;
+  const int c_stop = c_begin + (c_end - c_begin + D - 1) / D * D;
+  for (int cb = c_begin; cb < c_stop; cb += D) {
 #pragma unroll
-    for (int tau = 0; tau < ST; ++tau) {
-      const int t = c * ST + tau;
-      if (t >= t_end) break;
-      // backbone logits seed the accumulator: the MFMA chain yields z = U + B
-      const int s0 = 4 * tau + 2 * h;
-      const uint8_t* ru = &sU[b][(wave * 32 + n) * SEG];
-      float z[16];
-      decode16(*reinterpret_cast<const u32x4*>(ru + ((s0 ^ sw) * 16)),
-               *reinterpret_cast<const u32x4*>(ru + (((s0 + 1) ^ sw) * 16)), z);
-      f32x16 acc;
+    for (int d = 0; d < D; ++d) {
+      const int c = cb + d;
+      store_stage(d, c);
+      load_stage(d, c + D);
+      stage_barrier();  // stage c's W2 tiles visible to every wave
+      if (c < c_end) {
+        const uint8_t* ra_lds = sA[c & 1];
+        const uint8_t* ru_lds = &sR[wave][0][n * SEG];
+        const uint8_t* rt_lds = &sR[wave][NR - 1][n * SEG];
 #pragma unroll
-      for (int j = 0; j < 16; ++j) acc[j] = z[j];
-      const u32x4* At = reinterpret_cast<const u32x4*>(&sA[b][tau * kTileBytesA]) + lane;
+        for (int tau = 0; tau < ST; ++tau) {
+          const int t = c * ST + tau;
+          if (t < t_end) {
+            // backbone logits seed the accumulator: the MFMA chain yields z = U + B
+            const int s0 = 4 * tau + 2 * h;
+            float z[16];
+            decode16(*reinterpret_cast<const u32x4*>(ru_lds + ((s0 ^ sw) * 16)),
+                     *reinterpret_cast<const u32x4*>(ru_lds + (((s0 + 1) ^ sw) * 16)), z);
+            f32x16 acc;
 #pragma unroll
-      for (int s = 0; s < kSteps; ++s)
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(At[s * 64]), bop[s], acc, 0, 0, 0);
+            for (int j = 0; j < 16; ++j) acc[j] = z[j];
+            const u32x4* At = reinterpret_cast<const u32x4*>(ra_lds + tau * kTileBytesA) + lane;
 #pragma unroll
-      for (int j = 0; j < 16; ++j) z[j] = acc[j];
-      float tv[16];
-      if constexpr (kNeedT) {
-        const uint8_t* rt = &sT[b][(wave * 32 + n) * SEG];
-        decode16(*reinterpret_cast<const u32x4*>(rt + ((s0 ^ sw) * 16)),
-                 *reinterpret_cast<const u32x4*>(rt + (((s0 + 1) ^ sw) * 16)), tv);
+            for (int s = 0; s < kSteps; ++s)
+              acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(At[s * 64]), bop[s], acc, 0, 0, 0);
+#pragma unroll
+            for (int j = 0; j < 16; ++j) z[j] = acc[j];
+            float tv[16];
+            if constexpr (kNeedT)
+              decode16(*reinterpret_cast<const u32x4*>(rt_lds + ((s0 ^ sw) * 16)),
+                       *reinterpret_cast<const u32x4*>(rt_lds + (((s0 + 1) ^ sw) * 16)), tv);
+            epilogue<MODE>(st, z, tv, rc, t, t == t_begin, a.seed);
+          }
+        }
       }
-      epilogue<MODE>(st, z, tv, rc, t, t == t_begin, a.seed);
     }
   }
   finish<MODE>(st, rc, row, split, a, h == 0);
@@ -489,15 +480,13 @@ __global__ __launch_bounds__(kThreads) void k_bias_f32(const BiasPassArgs a) {
 }  // namespace
 
 // Vocabulary splits: enough workgroups for one full round on MI355X (256 CUs,
-// one 8-wave workgroup each), never more splits than pipeline stages.  The
-// draft pass (U only) stages 2 tiles (128-byte row segments); the verify
-// passes (U and T) stage 1 tile in a 3-deep ring.
+// one 8-wave workgroup each), never more splits than pipeline stages (2 tiles).
 BiasGeometry bias_geometry(int mode, int nrows, int V) {
   constexpr int kSlots = 256;
   BiasGeometry g;
   g.rows_per_block = kRowsPerBlock;
   g.row_blocks = (nrows + kRowsPerBlock - 1) / kRowsPerBlock;
-  g.tiles_per_stage = mode == kModeDraft ? 2 : 1;
+  g.tiles_per_stage = 2;
   const int ntiles = (V + kTile - 1) / kTile;
   const int nstages = (ntiles + g.tiles_per_stage - 1) / g.tiles_per_stage;
   g.nsplit = min(nstages, max(1, (kSlots + g.row_blocks - 1) / g.row_blocks));
@@ -509,13 +498,13 @@ hipError_t launch_bias_pass(int mode, bool bf16, const BiasPassArgs& a, hipStrea
   const dim3 grid(a.nsplit, (a.nrows + kRowsPerBlock - 1) / kRowsPerBlock);
   const dim3 block(kThreads);
   if (bf16 && a.vec_ok) {
-    if (mode == kModeDraft) hipLaunchKernelGGL((k_bias_bf16<kModeDraft, 2, 2, true>), grid, block, 0, stream, a);
-    else if (mode == kModeCstar) hipLaunchKernelGGL((k_bias_bf16<kModeCstar, 1, 3, true>), grid, block, 0, stream, a);
-    else hipLaunchKernelGGL((k_bias_bf16<kModeResidual, 1, 3, true>), grid, block, 0, stream, a);
+    if (mode == kModeDraft) hipLaunchKernelGGL((k_bias_bf16<kModeDraft, 3, true>), grid, block, 0, stream, a);
+    else if (mode == kModeCstar) hipLaunchKernelGGL((k_bias_bf16<kModeCstar, 2, true>), grid, block, 0, stream, a);
+    else hipLaunchKernelGGL((k_bias_bf16<kModeResidual, 2, true>), grid, block, 0, stream, a);
   } else if (bf16) {
-    if (mode == kModeDraft) hipLaunchKernelGGL((k_bias_bf16<kModeDraft, 2, 2, false>), grid, block, 0, stream, a);
-    else if (mode == kModeCstar) hipLaunchKernelGGL((k_bias_bf16<kModeCstar, 1, 3, false>), grid, block, 0, stream, a);
-    else hipLaunchKernelGGL((k_bias_bf16<kModeResidual, 1, 3, false>), grid, block, 0, stream, a);
+    if (mode == kModeDraft) hipLaunchKernelGGL((k_bias_bf16<kModeDraft, 3, false>), grid, block, 0, stream, a);
+    else if (mode == kModeCstar) hipLaunchKernelGGL((k_bias_bf16<kModeCstar, 2, false>), grid, block, 0, stream, a);
+    else hipLaunchKernelGGL((k_bias_bf16<kModeResidual, 2, false>), grid, block, 0, stream, a);
   } else {
     if (mode == kModeDraft) hipLaunchKernelGGL(k_bias_f32<kModeDraft>, grid, block, 0, stream, a);
     else if (mode == kModeCstar) hipLaunchKernelGGL(k_bias_f32<kModeCstar>, grid, block, 0, stream, a);

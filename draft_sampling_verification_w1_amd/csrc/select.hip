@@ -32,33 +32,41 @@ __device__ __forceinline__ int packed_slot(int j) {
   return (j & 3) | ((j >> 4) << 2) | (((j >> 2) & 3) << 3);
 }
 
-// sum_i w1[i] W2[i][v] in binary64, ranks in ascending order.
-__device__ double bias64(const void* W2p, bool bf16, const double* w1, int v) {
+// Partial bias sum_{i in [32p, 32p+32)} w1[i] W2[i][v] in binary64 (eight
+// threads per token; four independent 16-byte loads of the packed tile).
+__device__ double bias64_part(const void* W2p, bool bf16, const double* w1, int v, int p) {
   double acc = 0.0;
   if (bf16) {
     const u32x4* tile = reinterpret_cast<const u32x4*>(W2p) + (int64_t)(v >> 5) * (kSteps * 64);
     const int m = packed_slot(v & 31);
-    for (int q = 0; q < 2 * kSteps; ++q) {
-      const int hh = q / kSteps, s = q % kSteps;
-      const u32x4 c = tile[s * 64 + 32 * hh + m];
-      const double* w = w1 + 128 * hh + 8 * s;
-      acc = fma(w[0], (double)bf16_lo(c.x), acc);
-      acc = fma(w[1], (double)bf16_hi(c.x), acc);
-      acc = fma(w[2], (double)bf16_lo(c.y), acc);
-      acc = fma(w[3], (double)bf16_hi(c.y), acc);
-      acc = fma(w[4], (double)bf16_lo(c.z), acc);
-      acc = fma(w[5], (double)bf16_hi(c.z), acc);
-      acc = fma(w[6], (double)bf16_lo(c.w), acc);
-      acc = fma(w[7], (double)bf16_hi(c.w), acc);
+    const int hh = p >> 2, s0 = (p & 3) * 4;
+    u32x4 c[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) c[i] = tile[(s0 + i) * 64 + 32 * hh + m];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const double* w = w1 + 128 * hh + 8 * (s0 + i);
+      acc = fma(w[0], (double)bf16_lo(c[i].x), acc);
+      acc = fma(w[1], (double)bf16_hi(c[i].x), acc);
+      acc = fma(w[2], (double)bf16_lo(c[i].y), acc);
+      acc = fma(w[3], (double)bf16_hi(c[i].y), acc);
+      acc = fma(w[4], (double)bf16_lo(c[i].z), acc);
+      acc = fma(w[5], (double)bf16_hi(c[i].z), acc);
+      acc = fma(w[6], (double)bf16_lo(c[i].w), acc);
+      acc = fma(w[7], (double)bf16_hi(c[i].w), acc);
     }
   } else {
-    const f32x4* rowp = reinterpret_cast<const f32x4*>(W2p) + (int64_t)v * (kRank / 4);
-    for (int i4 = 0; i4 < kRank / 4; ++i4) {
-      const f32x4 c = rowp[i4];
-      acc = fma(w1[4 * i4 + 0], (double)c.x, acc);
-      acc = fma(w1[4 * i4 + 1], (double)c.y, acc);
-      acc = fma(w1[4 * i4 + 2], (double)c.z, acc);
-      acc = fma(w1[4 * i4 + 3], (double)c.w, acc);
+    const f32x4* rowp = reinterpret_cast<const f32x4*>(W2p) + (int64_t)v * (kRank / 4) + 8 * p;
+    f32x4 c[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) c[i] = rowp[i];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const double* w = w1 + 32 * p + 4 * i;
+      acc = fma(w[0], (double)c[i].x, acc);
+      acc = fma(w[1], (double)c[i].y, acc);
+      acc = fma(w[2], (double)c[i].z, acc);
+      acc = fma(w[3], (double)c[i].w, acc);
     }
   }
   return acc;
@@ -74,23 +82,32 @@ __device__ __forceinline__ double gumbel_at(uint64_t seed, uint32_t stream, int 
   return gumbel_f64(word_of(b, v & 3));
 }
 
-// Reductions over 256 threads (4 waves); every thread gets the result.
-__device__ double block_max(double x, double* sh) {
+// Block-wide (256 threads) max of four values / sum of one, every thread gets
+// the results.
+__device__ void block_max4(double* x, double (*sh)[4]) {
 #pragma unroll
-  for (int off = 1; off < 64; off <<= 1) x = fmax(x, __shfl_xor(x, off, 64));
+  for (int c = 0; c < 4; ++c)
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) x[c] = fmax(x[c], __shfl_xor(x[c], off, 64));
   __syncthreads();
-  if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = x;
+  if ((threadIdx.x & 63) == 0)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) sh[c][threadIdx.x >> 6] = x[c];
   __syncthreads();
-  return fmax(fmax(sh[0], sh[1]), fmax(sh[2], sh[3]));
+#pragma unroll
+  for (int c = 0; c < 4; ++c) x[c] = fmax(fmax(sh[c][0], sh[c][1]), fmax(sh[c][2], sh[c][3]));
+  __syncthreads();
 }
 
-__device__ double block_sum(double x, double* sh) {
+__device__ double block_sum(double x, double (*sh)[4]) {
 #pragma unroll
   for (int off = 1; off < 64; off <<= 1) x += __shfl_xor(x, off, 64);
   __syncthreads();
-  if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = x;
+  if ((threadIdx.x & 63) == 0) sh[0][threadIdx.x >> 6] = x;
   __syncthreads();
-  return (sh[0] + sh[1]) + (sh[2] + sh[3]);
+  const double r = (sh[0][0] + sh[0][1]) + (sh[0][2] + sh[0][3]);
+  __syncthreads();
+  return r;
 }
 
 struct SelRow {
@@ -102,18 +119,18 @@ struct SelRow {
   double ld, lt;  // residual: lse of p^d and p^t
 };
 
-// Log-weight of token v (< V) of the draw.
+// Log-weight of token v (< V) of the draw, given its bias (draft, residual).
 template <int MODE>
 __device__ __forceinline__ double log_weight(const SelectArgs& a, bool bf16, bool fallback,
-                                             const SelRow& q, const double* w1, int v) {
+                                             const SelRow& q, double bias, int v) {
   if constexpr (MODE == kSelDraft) {
-    return stored(a.U, bf16, q.uoff + v) + bias64(a.W2p, bf16, w1, v);
+    return stored(a.U, bf16, q.uoff + v) + bias;
   } else if constexpr (MODE == kSelBonus) {
     return stored(a.T, bf16, q.toff + v);
   } else {
     const double lpt = stored(a.T, bf16, q.toff + v) - q.lt;
     if (fallback) return lpt;
-    const double lpd = stored(a.U, bf16, q.uoff + v) + bias64(a.W2p, bf16, w1, v) - q.ld;
+    const double lpd = stored(a.U, bf16, q.uoff + v) + bias - q.ld;
     return lpt > lpd ? lpt + log1p(-exp(lpd - lpt)) : -INFINITY;
   }
 }
@@ -121,14 +138,15 @@ __device__ __forceinline__ double log_weight(const SelectArgs& a, bool bf16, boo
 template <int MODE>
 __global__ __launch_bounds__(kSelThreads) void k_select(const SelectArgs a, int bf16_flag) {
   __shared__ double w1s[kRank];
-  __shared__ double red[4];
+  __shared__ double red[4][4];
   __shared__ int cand[kMaxCand];
   __shared__ int ncand, overflow;
-  __shared__ double gsc[kSelThreads / 32];
-  __shared__ int gblk[kSelThreads / 32];
+  __shared__ double zc[32], zb[32];  // log-weights of the scored block and of the best block
+  __shared__ int bstar_sh;
   const bool bf16 = bf16_flag != 0;
   const int tid = threadIdx.x;
   const int i = blockIdx.x;
+  constexpr bool kBias = MODE != kSelBonus;
 
   SelRow q;
   q.rec = i;
@@ -153,7 +171,7 @@ __global__ __launch_bounds__(kSelThreads) void k_select(const SelectArgs a, int 
       q.toff = (int64_t)id * a.V;
     }
   }
-  if constexpr (MODE != kSelBonus) {
+  if constexpr (kBias) {
     const int x = (q.k == 1) ? a.anchors[q.r] : a.tokens[(int64_t)q.r * a.gamma + (q.k - 2)];
     q.prev = min(max(x, 0), a.V - 1);
     q.uoff = ((int64_t)q.r * a.gamma + (q.k - 1)) * a.V;
@@ -162,27 +180,31 @@ __global__ __launch_bounds__(kSelThreads) void k_select(const SelectArgs a, int 
   const int64_t rec0 = (int64_t)q.rec * a.nsplit;
   const uint32_t sblock = MODE == kSelDraft ? kStreamDraft : (MODE == kSelResidual ? kStreamResidual : kStreamBonus);
 
-  // 1. draft: log-sum-exp of the logits from the split partials
+  // 1. one pass over the split records: max logit (draft), largest lower
+  //    bounds of both record sets, residual mass (residual)
+  double mx[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+  double wsum = 0.0;
+  for (int j = tid; j < a.nsplit; j += kSelThreads) {
+    if constexpr (MODE == kSelDraft) mx[0] = fmax(mx[0], (double)a.pm[rec0 + j]);
+    mx[1] = fmax(mx[1], (double)a.cand.lo[rec0 + j]);
+    if constexpr (MODE == kSelResidual) {
+      mx[2] = fmax(mx[2], (double)a.cand_f.lo[rec0 + j]);
+      wsum += (double)a.wpos[rec0 + j];
+    }
+  }
+  block_max4(mx, red);
   double lse = 0.0;
   if constexpr (MODE == kSelDraft) {
-    double M = -INFINITY;
-    for (int j = tid; j < a.nsplit; j += kSelThreads) M = fmax(M, (double)a.pm[rec0 + j]);
-    M = block_max(M, red);
     double S = 0.0;
     for (int j = tid; j < a.nsplit; j += kSelThreads) {
       const float m = a.pm[rec0 + j];
-      if (m != -INFINITY) S += a.ps[rec0 + j] * exp((double)m - M);
+      if (m != -INFINITY) S += a.ps[rec0 + j] * exp((double)m - mx[0]);
     }
     S = block_sum(S, red);
-    lse = M + log(S);
+    lse = mx[0] + log(S);
   }
   bool fallback = false;
-  if constexpr (MODE == kSelResidual) {
-    double wsum = 0.0;
-    for (int j = tid; j < a.nsplit; j += kSelThreads) wsum += (double)a.wpos[rec0 + j];
-    wsum = block_sum(wsum, red);
-    fallback = !(wsum > 0.0);
-  }
+  if constexpr (MODE == kSelResidual) fallback = !(block_sum(wsum, red) > 0.0);
 
   int bstar = -1;
   for (int attempt = 0; attempt < 2 && bstar < 0; ++attempt) {
@@ -191,10 +213,8 @@ __global__ __launch_bounds__(kSelThreads) void k_select(const SelectArgs a, int 
       fallback = true;  // no block of the residual has binary64 mass: p^t instead
     }
     const BlockCands C = (MODE == kSelResidual && fallback) ? a.cand_f : a.cand;
-    // 2. largest lower bound
-    double Ls = -INFINITY;
-    for (int j = tid; j < a.nsplit; j += kSelThreads) Ls = fmax(Ls, (double)C.lo[rec0 + j]);
-    Ls = block_max(Ls, red);
+    const double Ls = (MODE == kSelResidual && fallback) ? mx[2] : mx[1];
+    // 2. blocks whose upper bound reaches the largest lower bound
     if (tid == 0) {
       ncand = 0;
       overflow = 0;
@@ -221,63 +241,55 @@ __global__ __launch_bounds__(kSelThreads) void k_select(const SelectArgs a, int 
     __syncthreads();
     const bool all = overflow != 0;
     const int total = all ? a.ntiles : min(ncand, kMaxCand);
-    // 3. binary64 block scores, 8 blocks at a time (32 threads per block)
-    const int g = tid >> 5, lj = tid & 31;
+    // 3. binary64 score of each such block: 8 threads per token for the bias,
+    //    then one wave takes the block's log-mass and Gumbel variate
+    const int tj = tid >> 3, tp = tid & 7;
     double best = -INFINITY;
     int bb = -1;
-    for (int base = 0; base < total; base += kSelThreads / 32) {
-      const int ci = base + g;
-      const int blk = ci < total ? (all ? ci : cand[ci]) : -1;
-      double w = -INFINITY;
-      if (blk >= 0) {
-        const int v = blk * kTile + lj;
-        if (v < a.V) w = log_weight<MODE>(a, bf16, fallback, q, w1s, v);
-      }
-      double m = w;
+    for (int ci = 0; ci < total; ++ci) {
+      const int blk = all ? ci : cand[ci];
+      const int v = blk * kTile + tj;
+      double part = 0.0;
+      if (kBias && v < a.V) part = bias64_part(a.W2p, bf16, w1s, v, tp);
+      part += __shfl_xor(part, 1, 64);
+      part += __shfl_xor(part, 2, 64);
+      part += __shfl_xor(part, 4, 64);
+      if (tp == 0) zc[tj] = v < a.V ? log_weight<MODE>(a, bf16, fallback, q, part, v) : -INFINITY;
+      __syncthreads();
+      if (tid < 32) {
+        const double w = zc[tid];
+        double m = w;
 #pragma unroll
-      for (int off = 1; off < 32; off <<= 1) m = fmax(m, __shfl_xor(m, off, 64));
-      double s = (m > -INFINITY) ? exp(w - m) : 0.0;
+        for (int off = 1; off < 32; off <<= 1) m = fmax(m, __shfl_xor(m, off, 64));
+        double s = (m > -INFINITY) ? exp(w - m) : 0.0;
 #pragma unroll
-      for (int off = 1; off < 32; off <<= 1) s += __shfl_xor(s, off, 64);
-      if (blk >= 0 && m > -INFINITY) {
-        const double sc = m + log(s) + gumbel_at(a.seed, sblock, q.r, q.k, (uint32_t)blk);
-        if (sc > best || (sc == best && blk < bb)) {
-          best = sc;
-          bb = blk;
+        for (int off = 1; off < 32; off <<= 1) s += __shfl_xor(s, off, 64);
+        if (m > -INFINITY) {
+          const double sc = m + log(s) + gumbel_at(a.seed, sblock, q.r, q.k, (uint32_t)blk);
+          if (bb < 0 || sc > best || (sc == best && blk < bb)) {
+            best = sc;
+            bb = blk;
+            zb[tid] = w;
+          }
         }
       }
+      __syncthreads();
     }
-    if (lj == 0) {
-      gsc[g] = best;
-      gblk[g] = bb;
-    }
+    if (tid == 0) bstar_sh = bb;
     __syncthreads();
-    if (tid == 0) {
-      double b = -INFINITY;
-      int k = -1;
-      for (int x = 0; x < kSelThreads / 32; ++x)
-        if (gblk[x] >= 0 && (gsc[x] > b || (gsc[x] == b && gblk[x] < k) || k < 0)) {
-          b = gsc[x];
-          k = gblk[x];
-        }
-      gblk[0] = k;
-    }
-    __syncthreads();
-    bstar = gblk[0];
+    bstar = bstar_sh;
     __syncthreads();
   }
 
-  // 4. member of the winning block
+  // 4. member of the winning block (its log-weights are in zb)
   if (tid < 32) {
     int x = -1;
     double wx = -INFINITY;
     if (bstar >= 0) {
       const int v = bstar * kTile + tid;
-      double w = -INFINITY, sc = -INFINITY;
-      if (v < a.V) {
-        w = log_weight<MODE>(a, bf16, fallback, q, w1s, v);
-        if (w > -INFINITY) sc = w + gumbel_at(a.seed, sblock + kMemberStream, q.r, q.k, (uint32_t)v);
-      }
+      const double w = zb[tid];
+      const double sc = (w > -INFINITY) ? w + gumbel_at(a.seed, sblock + kMemberStream, q.r, q.k, (uint32_t)v)
+                                        : -INFINITY;
       double bsc = sc;
       int bv = sc > -INFINITY ? v : -1;
 #pragma unroll
