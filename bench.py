@@ -13,6 +13,7 @@ starts.  Prints one JSON line.
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -21,6 +22,8 @@ import time
 import numpy as np
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+HERE = os.path.dirname(os.path.abspath(__file__))
+TRAFFIC_FILE = os.path.join(HERE, "profiles", "traffic.json")
 METRIC = "draft+verify positions/sec at V=151,936, R=256, γ=16; % HBM roofline"
 
 
@@ -70,6 +73,34 @@ def path_bytes(cfg, n_bonus):
     return draft + verify + outputs
 
 
+def measured_traffic(kernel):
+    """HBM bytes per launch of `kernel` from the committed counter summary
+    (FETCH_SIZE + WRITE_SIZE, scaled by a plain copy's reading), or None when
+    there is none or the kernel's source changed since it was taken."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+        ent = t["kernels"][kernel]
+        with open(os.path.join(HERE, ent["source"]), "rb") as f:
+            if hashlib.sha256(f.read()).hexdigest() != ent["source_sha256"]:
+                return None
+        return ent["bytes_per_launch"]
+    except (OSError, KeyError, ValueError):
+        return None
+
+
+def calibrate_copy(mb):
+    """A plain device copy of `mb` MiB (the reference kernel for the traffic counters)."""
+    import torch
+    n = mb << 20
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    log(f"[bench] copy calibration: 3 copies of {mb} MiB")
+
+
 def cpu_baseline(cfg, synth, inp, T, n_req):
     """The oracle (fp64 CPU) on the first n_req requests of the same workload."""
     from oracle import oracle as O
@@ -93,8 +124,10 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="high_concurrency")
-    ap.add_argument("--cpu-requests", type=int, default=32)
+    ap.add_argument("--cpu-requests", type=int, default=64)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="first run a plain device copy of MIB MiB (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -109,6 +142,8 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     dspark.lib()
+    if args.calibrate_copy:
+        calibrate_copy(args.calibrate_copy)
     tdt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
 
     def to_dev(a):
@@ -205,7 +240,7 @@ def main():
                    "path_hbm_frac": round(path_b / (ms * 1e-3) / (HBM_PEAK_GBS * 1e9), 4)},
         "roofline": {"kernel": dom, "bound": "hbm", "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": None, "bytes_per_launch": int(nb),
+                     "traffic": measured_traffic(dom), "bytes_per_launch": int(nb),
                      "avg_launch_us": round(avg_s * 1e6, 2)},
         "kernels_ms_per_step": {k: round(v[1], 4) for k, v in per_step.items()},
         "profiled_ms_per_step": round(prof_ms, 4),
