@@ -61,7 +61,9 @@ struct RowCtx {
   float eps;       // residual: relative error bound of the binary32 p^d, p^t
 };
 
-__device__ __forceinline__ RowCtx row_ctx(const BiasPassArgs& a, int i, int active_rows, bool bf16) {
+template <bool COH = false>
+__device__ __forceinline__ RowCtx row_ctx(const BiasPassArgs& a, int i, int active_rows, bool bf16,
+                                          int kpos) {
   RowCtx c;
   c.active = i < active_rows;
   c.r = 0;
@@ -78,9 +80,12 @@ __device__ __forceinline__ RowCtx row_ctx(const BiasPassArgs& a, int i, int acti
     c.k = id - c.r * a.gamma + 1;
   } else {
     c.r = i;
-    c.k = a.k;
+    c.k = kpos;
   }
-  int x = (c.k == 1) ? a.anchors[c.r] : a.tokens[(int64_t)c.r * a.gamma + (c.k - 2)];
+  const int32_t* tp = a.tokens + (int64_t)c.r * a.gamma + (c.k - 2);
+  int x = (c.k == 1) ? a.anchors[c.r]
+                     : (COH ? __hip_atomic_load(const_cast<int32_t*>(tp), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                            : *tp);
   c.prev = min(max(x, 0), a.V - 1);
   const size_t esz = bf16 ? 2 : 4;
   c.urow = (const char*)a.U + ((int64_t)c.r * a.gamma + (c.k - 1)) * (int64_t)a.V * esz;
@@ -247,24 +252,24 @@ __device__ __forceinline__ void epilogue(LaneState<MODE>& st, const float* z, co
 
 // Partial record of the split for the lane's row, written by the lower half of
 // the wave (both halves hold the same row; the c* sums are per half).
-template <int MODE>
+template <int MODE, bool COH = false>
 __device__ __forceinline__ void finish(const LaneState<MODE>& st, const RowCtx& rc, int row,
                                        int split, const BiasPassArgs& a, bool writer) {
   const int64_t o = (int64_t)row * a.nsplit + split;
   if constexpr (MODE == kModeDraft) {
     if (writer && rc.active) {
-      a.pm[o] = st.M;
-      a.ps[o] = st.S;
-      st.cand.store(a.cand, o);
+      store_to<COH>(a.pm + o, st.M);
+      store_to<COH>(a.ps + o, st.S);
+      st.cand.template store<COH>(a.cand, o);
     }
   } else if constexpr (MODE == kModeCstar) {
     const double s = st.s + xor32(st.s);
-    if (writer && rc.active) a.ps[o] = s;
+    if (writer && rc.active) store_to<COH>(a.ps + o, s);
   } else {
     if (writer && rc.active) {
-      st.cand.store(a.cand, o);
-      st.candf.store(a.cand_f, o);
-      a.wpos[o] = st.wpos;
+      st.cand.template store<COH>(a.cand, o);
+      st.candf.template store<COH>(a.cand_f, o);
+      store_to<COH>(a.wpos + o, st.wpos);
     }
   }
 }
@@ -278,8 +283,10 @@ __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast
 // tiles to a double-buffered workgroup area, the row segments to the wave's
 // own area (xor-swizzled 16-byte slots); one barrier per stage publishes the
 // W2 tiles.  VEC: rows 16-byte aligned (vector loads), else scalar loads.
-template <int MODE, int D, bool VEC>
-__global__ __launch_bounds__(kThreads) void k_bias_bf16(const BiasPassArgs a) {
+// One (split, row block) of a pass.  COH: the drafted tokens were written and
+// the records are read by other workgroups of the same kernel.
+template <int MODE, int D, bool VEC, bool COH>
+__device__ void bias_body(const BiasPassArgs& a, int split, int row_block, int kpos) {
   constexpr bool kNeedT = MODE != kModeDraft;
   constexpr int ST = 2;
   constexpr int SEG = ST * 64;     // bytes of one row per stage
@@ -295,16 +302,15 @@ __global__ __launch_bounds__(kThreads) void k_bias_bf16(const BiasPassArgs a) {
   const int n = lane & 31;
   const int h = lane >> 5;
   const int active_rows = a.row_count ? min(*a.row_count, a.nrows) : a.nrows;
-  const int row0 = blockIdx.y * kRowsPerBlock;
+  const int row0 = row_block * kRowsPerBlock;
   if (row0 >= active_rows) return;
-  const int split = blockIdx.x;
   const int t_begin = split_tile(split, a.nsplit, a.ntiles, ST);
   const int t_end = split_tile(split + 1, a.nsplit, a.ntiles, ST);
   const int c_begin = t_begin / ST;
   const int c_end = (t_end + ST - 1) / ST;
 
   const int row = row0 + wave * 32 + n;
-  const RowCtx rc = row_ctx(a, row, active_rows, true);
+  const RowCtx rc = row_ctx<COH>(a, row, active_rows, true, kpos);
   LaneState<MODE> st;
   st.init();
 
@@ -419,7 +425,12 @@ __global__ __launch_bounds__(kThreads) void k_bias_bf16(const BiasPassArgs a) {
       }
     }
   }
-  finish<MODE>(st, rc, row, split, a, h == 0);
+  finish<MODE, COH>(st, rc, row, split, a, h == 0);
+}
+
+template <int MODE, int D, bool VEC>
+__global__ __launch_bounds__(kThreads) void k_bias_bf16(const BiasPassArgs a) {
+  bias_body<MODE, D, VEC, false>(a, blockIdx.x, blockIdx.y, a.k);
 }
 
 // Binary32 rows: same row/lane layout, bias by VALU dot products against the
@@ -441,7 +452,7 @@ __global__ __launch_bounds__(kThreads) void k_bias_f32(const BiasPassArgs a) {
   constexpr bool kNeedT = MODE != kModeDraft;
 
   const int row = row0 + wave * 32 + n;
-  const RowCtx rc = row_ctx(a, row, active_rows, false);
+  const RowCtx rc = row_ctx(a, row, active_rows, false, a.k);
   LaneState<MODE> st;
   st.init();
   if (rc.active) {

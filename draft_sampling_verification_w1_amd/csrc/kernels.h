@@ -114,6 +114,7 @@ struct SelectArgs {
 };
 hipError_t launch_select(int mode, bool bf16, const SelectArgs& a, hipStream_t stream);
 
+
 // ---- verification helpers ------------------------------------------------
 struct VerifyWs {
   int32_t* row_ids;     // [R*gamma]

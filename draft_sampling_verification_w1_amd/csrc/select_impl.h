@@ -1,0 +1,342 @@
+// select_impl.h -- device code of the binary64 second stage of the two-level
+// Gumbel-max draws, as a workgroup-level function (one row per call).  See
+// select.hip for the method.
+#pragma once
+
+#include "device_common.h"
+#include "kernels.h"
+
+namespace dspark {
+namespace sel {
+
+constexpr int kMaxCand = 1024;
+
+// Position of tile-local token j among the 32 lanes of a packed W2 tile (the
+// inverse of the tile's token permutation).
+__device__ __forceinline__ int packed_slot(int j) {
+  return (j & 3) | ((j >> 4) << 2) | (((j >> 2) & 3) << 3);
+}
+
+// Partial bias sum_{i in [32p, 32p+32)} w1[i] W2[i][v] in binary64 (eight
+// threads per token; four independent 16-byte loads of the packed tile).
+__device__ double bias64_part(const void* W2p, bool bf16, const double* w1, int v, int p) {
+  double acc = 0.0;
+  if (bf16) {
+    const u32x4* tile = reinterpret_cast<const u32x4*>(W2p) + (int64_t)(v >> 5) * (kSteps * 64);
+    const int m = packed_slot(v & 31);
+    const int hh = p >> 2, s0 = (p & 3) * 4;
+    u32x4 c[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) c[i] = tile[(s0 + i) * 64 + 32 * hh + m];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const double* w = w1 + 128 * hh + 8 * (s0 + i);
+      acc = fma(w[0], (double)bf16_lo(c[i].x), acc);
+      acc = fma(w[1], (double)bf16_hi(c[i].x), acc);
+      acc = fma(w[2], (double)bf16_lo(c[i].y), acc);
+      acc = fma(w[3], (double)bf16_hi(c[i].y), acc);
+      acc = fma(w[4], (double)bf16_lo(c[i].z), acc);
+      acc = fma(w[5], (double)bf16_hi(c[i].z), acc);
+      acc = fma(w[6], (double)bf16_lo(c[i].w), acc);
+      acc = fma(w[7], (double)bf16_hi(c[i].w), acc);
+    }
+  } else {
+    const f32x4* rowp = reinterpret_cast<const f32x4*>(W2p) + (int64_t)v * (kRank / 4) + 8 * p;
+    f32x4 c[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) c[i] = rowp[i];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const double* w = w1 + 32 * p + 4 * i;
+      acc = fma(w[0], (double)c[i].x, acc);
+      acc = fma(w[1], (double)c[i].y, acc);
+      acc = fma(w[2], (double)c[i].z, acc);
+      acc = fma(w[3], (double)c[i].w, acc);
+    }
+  }
+  return acc;
+}
+
+// COH: loads of data written by other workgroups of the same kernel, which
+// must bypass the non-coherent per-XCD L2 (device-scope relaxed atomics).
+template <bool COH, typename T>
+__device__ __forceinline__ T ld(const T* p) {
+  if constexpr (COH) return __hip_atomic_load(const_cast<T*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  else return *p;
+}
+template <bool COH, typename T>
+__device__ __forceinline__ void st(T* p, T v) {
+  if constexpr (COH) __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  else *p = v;
+}
+
+__device__ __forceinline__ double stored(const void* p, bool bf16, int64_t i) {
+  return bf16 ? (double)bf16_at(reinterpret_cast<const uint16_t*>(p), i)
+              : (double)reinterpret_cast<const float*>(p)[i];
+}
+
+__device__ __forceinline__ double gumbel_at(uint64_t seed, uint32_t stream, int r, int k, uint32_t v) {
+  const u32x4 b = noise_block(seed, stream, (uint32_t)r, (uint32_t)k, v >> 2);
+  return gumbel_f64(word_of(b, v & 3));
+}
+
+// Block-wide max of four values / sum of one (blockDim.x = 64 * nw, nw <= 8);
+// every thread gets the results.
+__device__ void block_max4(double* x, double (*sh)[8]) {
+  const int nw = blockDim.x >> 6;
+#pragma unroll
+  for (int c = 0; c < 4; ++c)
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) x[c] = fmax(x[c], __shfl_xor(x[c], off, 64));
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) sh[c][threadIdx.x >> 6] = x[c];
+  __syncthreads();
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    double m = sh[c][0];
+    for (int w = 1; w < nw; ++w) m = fmax(m, sh[c][w]);
+    x[c] = m;
+  }
+  __syncthreads();
+}
+
+__device__ double block_sum(double x, double (*sh)[8]) {
+  const int nw = blockDim.x >> 6;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) x += __shfl_xor(x, off, 64);
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) sh[0][threadIdx.x >> 6] = x;
+  __syncthreads();
+  double r = sh[0][0];
+  for (int w = 1; w < nw; ++w) r += sh[0][w];
+  __syncthreads();
+  return r;
+}
+
+struct SelRow {
+  int rec;        // record row (index into the split records)
+  int r, k;       // request and 1-based position of the draw's random numbers
+  int prev;       // previous token (draft, residual)
+  int64_t uoff;   // element offset of the U row (draft, residual)
+  int64_t toff;   // element offset of the T row (residual, bonus)
+  double ld, lt;  // residual: lse of p^d and p^t
+};
+
+// Log-weight of token v (< V) of the draw, given its bias (draft, residual).
+template <int MODE>
+__device__ __forceinline__ double log_weight(const SelectArgs& a, bool bf16, bool fallback,
+                                             const SelRow& q, double bias, int v) {
+  if constexpr (MODE == kSelDraft) {
+    return stored(a.U, bf16, q.uoff + v) + bias;
+  } else if constexpr (MODE == kSelBonus) {
+    return stored(a.T, bf16, q.toff + v);
+  } else {
+    const double lpt = stored(a.T, bf16, q.toff + v) - q.lt;
+    if (fallback) return lpt;
+    const double lpd = stored(a.U, bf16, q.uoff + v) + bias - q.ld;
+    return lpt > lpd ? lpt + log1p(-exp(lpd - lpt)) : -INFINITY;
+  }
+}
+
+// Workgroup-shared state of one row's select.
+struct SelShared {
+  double w1s[kRank];
+  double red[4][8];
+  int cand[kMaxCand];
+  int ncand, overflow;
+  double zc[32], zb[32];  // log-weights of the scored block and of the best block
+  int bstar;
+};
+
+// The draw of row i (draft: request i at position a.k; residual / bonus: entry
+// i of the work list).  Any workgroup size 256..512; COH: split records and
+// drafted tokens were written by other workgroups of the same kernel.
+template <int MODE, bool COH>
+__device__ void select_row(const SelectArgs& a, int bf16_flag, int i, SelShared& sh, int kpos) {
+  double* const w1s = sh.w1s;
+  double (*red)[8] = sh.red;
+  int* const cand = sh.cand;
+  int& ncand = sh.ncand;
+  int& overflow = sh.overflow;
+  double* const zc = sh.zc;
+  double* const zb = sh.zb;
+  int& bstar_sh = sh.bstar;
+  const bool bf16 = bf16_flag != 0;
+  const int tid = threadIdx.x;
+  const int nt = blockDim.x;
+  constexpr bool kBias = MODE != kSelBonus;
+
+  SelRow q;
+  q.rec = i;
+  q.ld = q.lt = 0.0;
+  q.uoff = q.toff = 0;
+  q.prev = 0;
+  if constexpr (MODE == kSelDraft) {
+    q.r = i;
+    q.k = kpos;
+  } else {
+    if (i >= *a.row_count) return;
+    const int id = a.row_ids[i];
+    if constexpr (MODE == kSelResidual) {
+      q.r = id / a.gamma;
+      q.k = id - q.r * a.gamma + 1;
+      q.toff = ((int64_t)q.r * (a.gamma + 1) + (q.k - 1)) * a.V;
+      q.ld = a.lse_d[(int64_t)q.r * a.gamma + (q.k - 1)];
+      q.lt = a.lse_t[(int64_t)q.r * (a.gamma + 1) + (q.k - 1)];
+    } else {
+      q.r = id / (a.gamma + 1);
+      q.k = id - q.r * (a.gamma + 1) + 1;
+      q.toff = (int64_t)id * a.V;
+    }
+  }
+  if constexpr (kBias) {
+    const int x = (q.k == 1) ? a.anchors[q.r] : ld<COH>(a.tokens + (int64_t)q.r * a.gamma + (q.k - 2));
+    q.prev = min(max(x, 0), a.V - 1);
+    q.uoff = ((int64_t)q.r * a.gamma + (q.k - 1)) * a.V;
+    if (tid < kRank) w1s[tid] = stored(a.W1, bf16, (int64_t)q.prev * kRank + tid);
+  }
+  const int64_t rec0 = (int64_t)q.rec * a.nsplit;
+  const uint32_t sblock = MODE == kSelDraft ? kStreamDraft : (MODE == kSelResidual ? kStreamResidual : kStreamBonus);
+
+  // 1. one pass over the split records: max logit (draft), largest lower
+  //    bounds of both record sets, residual mass (residual)
+  double mx[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+  double wsum = 0.0;
+  for (int j = tid; j < a.nsplit; j += nt) {
+    if constexpr (MODE == kSelDraft) mx[0] = fmax(mx[0], (double)ld<COH>(a.pm + rec0 + j));
+    mx[1] = fmax(mx[1], (double)ld<COH>(a.cand.lo + rec0 + j));
+    if constexpr (MODE == kSelResidual) {
+      mx[2] = fmax(mx[2], (double)ld<COH>(a.cand_f.lo + rec0 + j));
+      wsum += (double)ld<COH>(a.wpos + rec0 + j);
+    }
+  }
+  block_max4(mx, red);
+  double lse = 0.0;
+  if constexpr (MODE == kSelDraft) {
+    double S = 0.0;
+    for (int j = tid; j < a.nsplit; j += nt) {
+      const float m = ld<COH>(a.pm + rec0 + j);
+      if (m != -INFINITY) S += ld<COH>(a.ps + rec0 + j) * exp((double)m - mx[0]);
+    }
+    S = block_sum(S, red);
+    lse = mx[0] + log(S);
+  }
+  bool fallback = false;
+  if constexpr (MODE == kSelResidual) fallback = !(block_sum(wsum, red) > 0.0);
+
+  int bstar = -1;
+  for (int attempt = 0; attempt < 2 && bstar < 0; ++attempt) {
+    if (attempt == 1) {
+      if (MODE != kSelResidual || fallback) break;
+      fallback = true;  // no block of the residual has binary64 mass: p^t instead
+    }
+    const BlockCands C = (MODE == kSelResidual && fallback) ? a.cand_f : a.cand;
+    const double Ls = (MODE == kSelResidual && fallback) ? mx[2] : mx[1];
+    // 2. blocks whose upper bound reaches the largest lower bound
+    if (tid == 0) {
+      ncand = 0;
+      overflow = 0;
+    }
+    __syncthreads();
+    for (int j = tid; j < a.nsplit; j += nt) {
+      const double h1 = ld<COH>(C.hi1 + rec0 + j), h2 = ld<COH>(C.hi2 + rec0 + j);
+      const int b1 = ld<COH>(C.b1 + rec0 + j);
+      if (h2 > -INFINITY && h2 >= Ls) {
+        const int t0 = split_tile(j, a.nsplit, a.ntiles, a.tiles_per_stage);
+        const int t1 = split_tile(j + 1, a.nsplit, a.ntiles, a.tiles_per_stage);
+        const int pos = atomicAdd(&ncand, t1 - t0);
+        if (pos + (t1 - t0) <= kMaxCand) {
+          for (int t = t0; t < t1; ++t) cand[pos + t - t0] = t;
+        } else {
+          overflow = 1;
+        }
+      } else if (h1 > -INFINITY && h1 >= Ls && b1 >= 0) {
+        const int pos = atomicAdd(&ncand, 1);
+        if (pos < kMaxCand) cand[pos] = b1;
+        else overflow = 1;
+      }
+    }
+    __syncthreads();
+    const bool all = overflow != 0;
+    const int total = all ? a.ntiles : min(ncand, kMaxCand);
+    // 3. binary64 score of each such block: 8 threads per token for the bias,
+    //    then one wave takes the block's log-mass and Gumbel variate
+    const int tj = tid >> 3, tp = tid & 7;
+    double best = -INFINITY;
+    int bb = -1;
+    for (int ci = 0; ci < total; ++ci) {
+      const int blk = all ? ci : cand[ci];
+      const int v = blk * kTile + tj;
+      double part = 0.0;
+      if (kBias && tid < 256 && v < a.V) part = bias64_part(a.W2p, bf16, w1s, v, tp);
+      part += __shfl_xor(part, 1, 64);
+      part += __shfl_xor(part, 2, 64);
+      part += __shfl_xor(part, 4, 64);
+      if (tid < 256 && tp == 0) zc[tj] = v < a.V ? log_weight<MODE>(a, bf16, fallback, q, part, v) : -INFINITY;
+      __syncthreads();
+      if (tid < 32) {
+        const double w = zc[tid];
+        double m = w;
+#pragma unroll
+        for (int off = 1; off < 32; off <<= 1) m = fmax(m, __shfl_xor(m, off, 64));
+        double s = (m > -INFINITY) ? exp(w - m) : 0.0;
+#pragma unroll
+        for (int off = 1; off < 32; off <<= 1) s += __shfl_xor(s, off, 64);
+        if (m > -INFINITY) {
+          const double sc = m + log(s) + gumbel_at(a.seed, sblock, q.r, q.k, (uint32_t)blk);
+          if (bb < 0 || sc > best || (sc == best && blk < bb)) {
+            best = sc;
+            bb = blk;
+            zb[tid] = w;
+          }
+        }
+      }
+      __syncthreads();
+    }
+    if (tid == 0) bstar_sh = bb;
+    __syncthreads();
+    bstar = bstar_sh;
+    __syncthreads();
+  }
+
+  // 4. member of the winning block (its log-weights are in zb)
+  if (tid < 32) {
+    int x = -1;
+    double wx = -INFINITY;
+    if (bstar >= 0) {
+      const int v = bstar * kTile + tid;
+      const double w = zb[tid];
+      const double sc = (w > -INFINITY) ? w + gumbel_at(a.seed, sblock + kMemberStream, q.r, q.k, (uint32_t)v)
+                                        : -INFINITY;
+      double bsc = sc;
+      int bv = sc > -INFINITY ? v : -1;
+#pragma unroll
+      for (int off = 1; off < 32; off <<= 1) {
+        const double s2 = __shfl_xor(bsc, off, 64);
+        const int v2 = __shfl_xor(bv, off, 64);
+        if (v2 >= 0 && (bv < 0 || s2 > bsc || (s2 == bsc && v2 < bv))) {
+          bsc = s2;
+          bv = v2;
+        }
+      }
+      x = bv;
+      wx = __shfl(w, x >= 0 ? x - bstar * kTile : 0, 64);
+    }
+    if (tid == 0) {
+      if constexpr (MODE == kSelDraft) {
+        const int64_t o = (int64_t)q.r * a.gamma + (q.k - 1);
+        st<COH>(a.out_tokens + o, x);
+        a.out_lse[o] = lse;
+        a.out_logq[o] = wx - lse;
+      } else {
+        a.out_tokens[q.r] = x;
+      }
+    }
+  }
+}
+
+
+}  // namespace sel
+}  // namespace dspark
