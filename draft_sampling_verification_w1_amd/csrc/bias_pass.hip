@@ -35,6 +35,10 @@ constexpr int kRowsPerBlock = kWaves * 32;
 constexpr int kThreads = kWaves * 64;
 constexpr int kTileBytesA = kSteps * 64 * 16;  // one packed W2 tile (16 KB)
 
+// s_waitcnt immediate for "at most n vector-memory loads outstanding" (gfx9
+// encoding: vmcnt in bits [3:0] and [15:14]; expcnt and lgkmcnt left free).
+constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | 0x0F70; }
+
 // Workgroup barrier of the stage loop: LDS stores complete, then s_barrier.
 // __syncthreads' release fence would also wait for the register prefetches of
 // later stages that are still in flight.
@@ -277,7 +281,7 @@ __device__ __forceinline__ void finish(const LaneState<MODE>& st, const RowCtx& 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
 // One pipeline stage = 2 tiles (64 tokens).  Every wave prefetches D stages
-// ahead into registers: its 1/8 share of the stage's packed W2 tiles (4 x 16 B
+// (2 measured best) ahead into registers: its 1/8 share of the stage's packed W2 tiles (4 x 16 B
 // per lane) and the 128-byte segments of its own 32 rows of U (and T), 8 rows
 // x 128 B per load instruction.  At its turn a stage is written to LDS: the W2
 // tiles to a double-buffered workgroup area, the row segments to the wave's
@@ -293,6 +297,8 @@ __device__ void bias_body(const BiasPassArgs& a, int split, int row_block, int k
   constexpr int NSEG = SEG / 16;   // 16-byte segments of one row per stage
   constexpr int kABytes = ST * kTileBytesA;
   constexpr int NR = kNeedT ? 2 : 1;
+  // the draft has the registers to batch the A-fragment reads of a tile
+  constexpr bool kBatchA = !kNeedT;
   __shared__ __attribute__((aligned(16))) uint8_t sA[2][kABytes];
   __shared__ __attribute__((aligned(16))) uint8_t sR[kWaves][NR][32 * SEG];
 
@@ -372,16 +378,23 @@ __device__ void bias_body(const BiasPassArgs& a, int split, int row_block, int k
     }
   };
 
-#pragma unroll
-  for (int d = 0; d < D; ++d) load_stage(d, c_begin + d);
-  // the W1 gather waits on the previous token; it is issued after the first
-  // stages' loads so that their latency overlaps that chain
+  // Stage 0's loads, then the W1 gather (which waits on the previous token),
+  // then the later stages; one explicit wait leaves exactly the later stages in
+  // flight.  The compiler sees the wait, so the loop needs no further wait for
+  // the W1 rows (otherwise every tile drains the prefetch).
+  load_stage(0, c_begin);
   bf16x8 bop[kSteps];
   {
     const u32x4* w1 = reinterpret_cast<const u32x4*>(
         reinterpret_cast<const uint16_t*>(a.W1) + (int64_t)rc.prev * kRank + 128 * h);
 #pragma unroll
     for (int s = 0; s < kSteps; ++s) bop[s] = as_bf16x8(rc.active ? w1[s] : (u32x4){0u, 0u, 0u, 0u});
+  }
+#pragma unroll
+  for (int d = 1; d < D; ++d) load_stage(d, c_begin + d);
+  {
+    constexpr int kLoadsPerStage = 4 * (kNeedT ? 3 : 2);
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(kLoadsPerStage * (D - 1)));
   }
 
   const int sw = seg_swz<NSEG>(n);
@@ -410,9 +423,21 @@ __device__ void bias_body(const BiasPassArgs& a, int split, int row_block, int k
 #pragma unroll
             for (int j = 0; j < 16; ++j) acc[j] = z[j];
             const u32x4* At = reinterpret_cast<const u32x4*>(ra_lds + tau * kTileBytesA) + lane;
+            if constexpr (kBatchA) {
+              // all 16 A fragments in flight before the chain starts (one LDS
+              // latency per tile instead of one per MFMA pair)
+              u32x4 av[kSteps];
 #pragma unroll
-            for (int s = 0; s < kSteps; ++s)
-              acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(At[s * 64]), bop[s], acc, 0, 0, 0);
+              for (int s = 0; s < kSteps; ++s) av[s] = At[s * 64];
+              __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+              for (int s = 0; s < kSteps; ++s)
+                acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(av[s]), bop[s], acc, 0, 0, 0);
+            } else {
+#pragma unroll
+              for (int s = 0; s < kSteps; ++s)
+                acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(At[s * 64]), bop[s], acc, 0, 0, 0);
+            }
 #pragma unroll
             for (int j = 0; j < 16; ++j) z[j] = acc[j];
             float tv[16];
@@ -509,11 +534,11 @@ hipError_t launch_bias_pass(int mode, bool bf16, const BiasPassArgs& a, hipStrea
   const dim3 grid(a.nsplit, (a.nrows + kRowsPerBlock - 1) / kRowsPerBlock);
   const dim3 block(kThreads);
   if (bf16 && a.vec_ok) {
-    if (mode == kModeDraft) hipLaunchKernelGGL((k_bias_bf16<kModeDraft, 3, true>), grid, block, 0, stream, a);
+    if (mode == kModeDraft) hipLaunchKernelGGL((k_bias_bf16<kModeDraft, 2, true>), grid, block, 0, stream, a);
     else if (mode == kModeCstar) hipLaunchKernelGGL((k_bias_bf16<kModeCstar, 2, true>), grid, block, 0, stream, a);
     else hipLaunchKernelGGL((k_bias_bf16<kModeResidual, 2, true>), grid, block, 0, stream, a);
   } else if (bf16) {
-    if (mode == kModeDraft) hipLaunchKernelGGL((k_bias_bf16<kModeDraft, 3, false>), grid, block, 0, stream, a);
+    if (mode == kModeDraft) hipLaunchKernelGGL((k_bias_bf16<kModeDraft, 2, false>), grid, block, 0, stream, a);
     else if (mode == kModeCstar) hipLaunchKernelGGL((k_bias_bf16<kModeCstar, 2, false>), grid, block, 0, stream, a);
     else hipLaunchKernelGGL((k_bias_bf16<kModeResidual, 2, false>), grid, block, 0, stream, a);
   } else {
