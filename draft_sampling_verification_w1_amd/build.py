@@ -26,6 +26,14 @@ HIPCC_FLAGS = [
 ]
 
 
+# Per-source flags.  The split passes never produce or test a NaN (entries
+# outside the vocabulary are -inf, and a block whose maximum is -inf is left
+# before any difference of infinities is formed); without NaNs to honour, the
+# compiler drops the NaN-quieting v_max it otherwise puts in front of every
+# maximum of matrix-core results.
+EXTRA_FLAGS = {"bias_pass.hip": ["-fno-honor-nans"]}
+
+
 def _hipcc() -> str:
     for c in (os.environ.get("HIPCC"), shutil.which("hipcc"), "/opt/rocm/bin/hipcc"):
         if c and os.path.exists(c):
@@ -35,7 +43,7 @@ def _hipcc() -> str:
 
 def _compile(src: str) -> str:
     obj = os.path.join(OBJDIR, os.path.splitext(src)[0] + ".o")
-    cmd = [_hipcc(), *HIPCC_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [_hipcc(), *HIPCC_FLAGS, *EXTRA_FLAGS.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stderr}")

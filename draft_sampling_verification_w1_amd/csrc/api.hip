@@ -194,6 +194,7 @@ size_t packed_bytes(const dspark_problem* p) {
 struct TimingRecord {
   const char* name;
   hipEvent_t start, stop;
+  bool stopped;  // the stop event was recorded
 };
 
 std::mutex g_timing_mu;
@@ -227,7 +228,7 @@ namespace dspark {
 TimingScope::TimingScope(const char* name, hipStream_t stream) : slot_(-1), stream_(stream) {
   std::lock_guard<std::mutex> lock(g_timing_mu);
   if (!g_timing_on) return;
-  TimingRecord r{name, pooled_event(), pooled_event()};
+  TimingRecord r{name, pooled_event(), pooled_event(), false};
   if (!r.start || !r.stop || hipEventRecord(r.start, stream) != hipSuccess) return;
   g_timing_recs.push_back(r);
   slot_ = (int)g_timing_recs.size() - 1;
@@ -236,7 +237,10 @@ TimingScope::TimingScope(const char* name, hipStream_t stream) : slot_(-1), stre
 TimingScope::~TimingScope() {
   if (slot_ < 0) return;
   std::lock_guard<std::mutex> lock(g_timing_mu);
-  if (slot_ < (int)g_timing_recs.size()) hipEventRecord(g_timing_recs[slot_].stop, stream_);
+  if (slot_ < (int)g_timing_recs.size()) {
+    TimingRecord& r = g_timing_recs[slot_];
+    r.stopped = hipEventRecord(r.stop, stream_) == hipSuccess;
+  }
 }
 
 }  // namespace dspark
@@ -255,6 +259,7 @@ __attribute__((visibility("default"))) int dspark_timing_report(char* buf, size_
   std::map<std::string, std::pair<long, double>> agg;
   std::vector<std::string> order;
   for (auto& r : g_timing_recs) {
+    if (!r.stopped) return hip_fail(hipErrorInvalidValue, "timing report: a stop event was not recorded");
     hipError_t e = hipEventSynchronize(r.stop);
     if (e != hipSuccess) return hip_fail(e, "timing report");
     float ms = 0.f;

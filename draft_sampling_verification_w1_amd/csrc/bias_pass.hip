@@ -199,15 +199,13 @@ __device__ __forceinline__ void epilogue(LaneState<MODE>& st, const float* z, co
                                          const RowCtx& rc, int t, bool first, uint64_t seed) {
   if constexpr (MODE == kModeDraft) {
     if (first || (t & 3) == 0) st.words = noise_block(seed, kStreamDraft, rc.r, rc.k, (uint32_t)t >> 2);
-    const float ml = max16(z);
-    const float mt = fmaxf(ml, xor32(ml));
+    const float mt = max_halves(max16(z));
     if (mt == -INFINITY) return;  // block without mass
     const float mt2 = mt * kLog2e;
     float e[16];
 #pragma unroll
     for (int j = 0; j < 16; ++j) e[j] = __builtin_amdgcn_exp2f(fmaf(z[j], kLog2e, -mt2));
-    const float sl = sum16(e);
-    const float s = sl + xor32(sl);
+    const float s = sum_halves(sum16(e));
     if (mt > st.M) {
       st.S = st.S * (double)__builtin_amdgcn_exp2f((st.M - mt) * kLog2e) + (double)s;
       st.M = mt;
@@ -233,9 +231,9 @@ __device__ __forceinline__ void epilogue(LaneState<MODE>& st, const float* z, co
       p += pt + pd;
       q += pt;
     }
-    const float W = w + xor32(w);
-    const float P = p + xor32(p);
-    const float Q = q + xor32(q);
+    const float W = sum_halves(w);
+    const float P = sum_halves(p);
+    const float Q = sum_halves(q);
     if (first || (t & 3) == 0) st.words = noise_block(seed, kStreamResidual, rc.r, rc.k, (uint32_t)t >> 2);
     const float g = gumbel_f32(word_of(st.words, t & 3));
     constexpr float kG = 0x1p-13f;  // Gumbel and log2 rounding

@@ -200,6 +200,20 @@ __device__ __forceinline__ T xor32(T v) {
   return __shfl_xor(v, 32, 64);
 }
 
+// Lane l combined with lane l ^ 32 in one v_permlane32_swap (a VALU op, no LDS
+// round trip).  Given the same value twice, the builtin returns the lower
+// half's values in every lane of its first result and the upper half's in its
+// second, so the pair is {x[l], x[l ^ 32]} in some order; max and sum are
+// symmetric, so every lane gets the same bits as with xor32.
+__device__ __forceinline__ float max_halves(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_halves(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // ---------------------------------------------------------------------------
 // Partial records written per (vocabulary split, row) and merged later.
 // Arrays are structure-of-arrays with row stride `ld` (the row capacity).

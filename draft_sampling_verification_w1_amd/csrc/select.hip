@@ -32,6 +32,9 @@ __global__ __launch_bounds__(256) void k_select(const SelectArgs a, int bf16_fla
 
 hipError_t launch_select(int mode, bool bf16, const SelectArgs& a, hipStream_t stream) {
   const int flag = bf16 ? 1 : 0;
+  // each of the 256 threads holds at most RecSlots<MODE>::K split records
+  const int max_splits = 256 * (mode == kSelBonus ? sel::RecSlots<kSelBonus>::K : 1);
+  if (a.nsplit < 1 || a.nsplit > max_splits) return hipErrorInvalidValue;
   if (mode == kSelDraft) {
     TimingScope timing("draft_select", stream);
     hipLaunchKernelGGL(k_select<kSelDraft>, dim3(a.R), dim3(256), 0, stream, a, flag);

@@ -17,41 +17,51 @@ __device__ __forceinline__ int packed_slot(int j) {
   return (j & 3) | ((j >> 4) << 2) | (((j >> 2) & 3) << 3);
 }
 
-// Partial bias sum_{i in [32p, 32p+32)} w1[i] W2[i][v] in binary64 (eight
-// threads per token; four independent 16-byte loads of the packed tile).
-__device__ double bias64_part(const void* W2p, bool bf16, const double* w1, int v, int p) {
-  double acc = 0.0;
+// Partial bias sum_{i in [32p, 32p+32)} w1[i] W2[i][v] in binary64, eight
+// threads per token, as two steps so that the loads of a block (and of its
+// stored logits) are all in flight before any arithmetic waits on them.
+struct BiasLoad {
+  u32x4 c[8];  // bf16: 4 packed-tile chunks; binary32: 8 chunks of the row
+};
+
+__device__ __forceinline__ void bias64_load(BiasLoad& L, const void* W2p, bool bf16, int v, int p) {
   if (bf16) {
     const u32x4* tile = reinterpret_cast<const u32x4*>(W2p) + (int64_t)(v >> 5) * (kSteps * 64);
     const int m = packed_slot(v & 31);
     const int hh = p >> 2, s0 = (p & 3) * 4;
-    u32x4 c[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) c[i] = tile[(s0 + i) * 64 + 32 * hh + m];
+    for (int i = 0; i < 4; ++i) L.c[i] = tile[(s0 + i) * 64 + 32 * hh + m];
+  } else {
+    const u32x4* rowp = reinterpret_cast<const u32x4*>(W2p) + (int64_t)v * (kRank / 4) + 8 * p;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) L.c[i] = rowp[i];
+  }
+}
+
+__device__ __forceinline__ double bias64_dot(const BiasLoad& L, bool bf16, const double* w1, int p) {
+  double acc = 0.0;
+  if (bf16) {
+    const int hh = p >> 2, s0 = (p & 3) * 4;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const double* w = w1 + 128 * hh + 8 * (s0 + i);
-      acc = fma(w[0], (double)bf16_lo(c[i].x), acc);
-      acc = fma(w[1], (double)bf16_hi(c[i].x), acc);
-      acc = fma(w[2], (double)bf16_lo(c[i].y), acc);
-      acc = fma(w[3], (double)bf16_hi(c[i].y), acc);
-      acc = fma(w[4], (double)bf16_lo(c[i].z), acc);
-      acc = fma(w[5], (double)bf16_hi(c[i].z), acc);
-      acc = fma(w[6], (double)bf16_lo(c[i].w), acc);
-      acc = fma(w[7], (double)bf16_hi(c[i].w), acc);
+      acc = fma(w[0], (double)bf16_lo(L.c[i].x), acc);
+      acc = fma(w[1], (double)bf16_hi(L.c[i].x), acc);
+      acc = fma(w[2], (double)bf16_lo(L.c[i].y), acc);
+      acc = fma(w[3], (double)bf16_hi(L.c[i].y), acc);
+      acc = fma(w[4], (double)bf16_lo(L.c[i].z), acc);
+      acc = fma(w[5], (double)bf16_hi(L.c[i].z), acc);
+      acc = fma(w[6], (double)bf16_lo(L.c[i].w), acc);
+      acc = fma(w[7], (double)bf16_hi(L.c[i].w), acc);
     }
   } else {
-    const f32x4* rowp = reinterpret_cast<const f32x4*>(W2p) + (int64_t)v * (kRank / 4) + 8 * p;
-    f32x4 c[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) c[i] = rowp[i];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const double* w = w1 + 32 * p + 4 * i;
-      acc = fma(w[0], (double)c[i].x, acc);
-      acc = fma(w[1], (double)c[i].y, acc);
-      acc = fma(w[2], (double)c[i].z, acc);
-      acc = fma(w[3], (double)c[i].w, acc);
+      acc = fma(w[0], (double)__uint_as_float(L.c[i].x), acc);
+      acc = fma(w[1], (double)__uint_as_float(L.c[i].y), acc);
+      acc = fma(w[2], (double)__uint_as_float(L.c[i].z), acc);
+      acc = fma(w[3], (double)__uint_as_float(L.c[i].w), acc);
     }
   }
   return acc;
@@ -124,21 +134,30 @@ struct SelRow {
   double ld, lt;  // residual: lse of p^d and p^t
 };
 
-// Log-weight of token v (< V) of the draw, given its bias (draft, residual).
+// Log-weight of a token of the draw from its stored logits (u: U, t: T) and
+// its bias (draft, residual).
 template <int MODE>
-__device__ __forceinline__ double log_weight(const SelectArgs& a, bool bf16, bool fallback,
-                                             const SelRow& q, double bias, int v) {
+__device__ __forceinline__ double log_weight(bool fallback, const SelRow& q, double u, double t,
+                                             double bias) {
   if constexpr (MODE == kSelDraft) {
-    return stored(a.U, bf16, q.uoff + v) + bias;
+    return u + bias;
   } else if constexpr (MODE == kSelBonus) {
-    return stored(a.T, bf16, q.toff + v);
+    return t;
   } else {
-    const double lpt = stored(a.T, bf16, q.toff + v) - q.lt;
+    const double lpt = t - q.lt;
     if (fallback) return lpt;
-    const double lpd = stored(a.U, bf16, q.uoff + v) + bias - q.ld;
+    const double lpd = u + bias - q.ld;
     return lpt > lpd ? lpt + log1p(-exp(lpd - lpt)) : -INFINITY;
   }
 }
+
+// Split records held per thread: split j lives in thread j % nt, slot j / nt.
+// Draft and residual passes have at most 256 splits (one per thread), the
+// bonus pass up to 2048.
+template <int MODE>
+struct RecSlots {
+  static constexpr int K = MODE == kSelBonus ? 8 : 1;
+};
 
 // Workgroup-shared state of one row's select.
 struct SelShared {
@@ -146,40 +165,38 @@ struct SelShared {
   double red[4][8];
   int cand[kMaxCand];
   int ncand, overflow;
-  double zc[32], zb[32];  // log-weights of the scored block and of the best block
+  double zc[32], gc[32];  // scored block: log-weights and member Gumbel variates
+  double zb[32], gb[32];  // best block so far
   int bstar;
 };
 
 // The draw of row i (draft: request i at position a.k; residual / bonus: entry
-// i of the work list).  Any workgroup size 256..512; COH: split records and
-// drafted tokens were written by other workgroups of the same kernel.
+// i of the work list).  blockDim.x = 256; COH: split records and drafted tokens
+// were written by other workgroups of the same kernel.
 template <int MODE, bool COH>
 __device__ void select_row(const SelectArgs& a, int bf16_flag, int i, SelShared& sh, int kpos) {
+  constexpr int K = RecSlots<MODE>::K;
+  constexpr bool kDraft = MODE == kSelDraft;
+  constexpr bool kResid = MODE == kSelResidual;
+  constexpr bool kBias = MODE != kSelBonus;
   double* const w1s = sh.w1s;
   double (*red)[8] = sh.red;
-  int* const cand = sh.cand;
-  int& ncand = sh.ncand;
-  int& overflow = sh.overflow;
-  double* const zc = sh.zc;
-  double* const zb = sh.zb;
-  int& bstar_sh = sh.bstar;
   const bool bf16 = bf16_flag != 0;
   const int tid = threadIdx.x;
   const int nt = blockDim.x;
-  constexpr bool kBias = MODE != kSelBonus;
 
   SelRow q;
   q.rec = i;
   q.ld = q.lt = 0.0;
   q.uoff = q.toff = 0;
   q.prev = 0;
-  if constexpr (MODE == kSelDraft) {
+  if constexpr (kDraft) {
     q.r = i;
     q.k = kpos;
   } else {
     if (i >= *a.row_count) return;
     const int id = a.row_ids[i];
-    if constexpr (MODE == kSelResidual) {
+    if constexpr (kResid) {
       q.r = id / a.gamma;
       q.k = id - q.r * a.gamma + 1;
       q.toff = ((int64_t)q.r * (a.gamma + 1) + (q.k - 1)) * a.V;
@@ -198,86 +215,128 @@ __device__ void select_row(const SelectArgs& a, int bf16_flag, int i, SelShared&
     if (tid < kRank) w1s[tid] = stored(a.W1, bf16, (int64_t)q.prev * kRank + tid);
   }
   const int64_t rec0 = (int64_t)q.rec * a.nsplit;
-  const uint32_t sblock = MODE == kSelDraft ? kStreamDraft : (MODE == kSelResidual ? kStreamResidual : kStreamBonus);
+  const uint32_t sblock = kDraft ? kStreamDraft : (kResid ? kStreamResidual : kStreamBonus);
 
-  // 1. one pass over the split records: max logit (draft), largest lower
-  //    bounds of both record sets, residual mass (residual)
-  double mx[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+  // 1. every field of the thread's split records in one batch of loads
+  float pm[K], lo[K], h1[K], h2[K], lof[K], h1f[K], h2f[K];
+  double ps[K];
+  int b1[K], b1f[K];
   double wsum = 0.0;
-  for (int j = tid; j < a.nsplit; j += nt) {
-    if constexpr (MODE == kSelDraft) mx[0] = fmax(mx[0], (double)ld<COH>(a.pm + rec0 + j));
-    mx[1] = fmax(mx[1], (double)ld<COH>(a.cand.lo + rec0 + j));
-    if constexpr (MODE == kSelResidual) {
-      mx[2] = fmax(mx[2], (double)ld<COH>(a.cand_f.lo + rec0 + j));
-      wsum += (double)ld<COH>(a.wpos + rec0 + j);
+#pragma unroll
+  for (int s = 0; s < K; ++s) {
+    const int j = tid + s * nt;
+    const bool has = j < a.nsplit;
+    const int64_t o = rec0 + (has ? j : 0);
+    pm[s] = lo[s] = h1[s] = h2[s] = lof[s] = h1f[s] = h2f[s] = -INFINITY;
+    ps[s] = 0.0;
+    b1[s] = b1f[s] = -1;
+    if (has) {
+      lo[s] = ld<COH>(a.cand.lo + o);
+      h1[s] = ld<COH>(a.cand.hi1 + o);
+      h2[s] = ld<COH>(a.cand.hi2 + o);
+      b1[s] = ld<COH>(a.cand.b1 + o);
+      if constexpr (kDraft) {
+        pm[s] = ld<COH>(a.pm + o);
+        ps[s] = ld<COH>(a.ps + o);
+      }
+      if constexpr (kResid) {
+        lof[s] = ld<COH>(a.cand_f.lo + o);
+        h1f[s] = ld<COH>(a.cand_f.hi1 + o);
+        h2f[s] = ld<COH>(a.cand_f.hi2 + o);
+        b1f[s] = ld<COH>(a.cand_f.b1 + o);
+        wsum += (double)ld<COH>(a.wpos + o);
+      }
     }
+  }
+
+  // 2. max logit (draft), largest lower bounds of both record sets, residual
+  //    mass (residual)
+  double mx[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+#pragma unroll
+  for (int s = 0; s < K; ++s) {
+    mx[0] = fmax(mx[0], (double)pm[s]);
+    mx[1] = fmax(mx[1], (double)lo[s]);
+    mx[2] = fmax(mx[2], (double)lof[s]);
   }
   block_max4(mx, red);
   double lse = 0.0;
-  if constexpr (MODE == kSelDraft) {
+  if constexpr (kDraft) {
     double S = 0.0;
-    for (int j = tid; j < a.nsplit; j += nt) {
-      const float m = ld<COH>(a.pm + rec0 + j);
-      if (m != -INFINITY) S += ld<COH>(a.ps + rec0 + j) * exp((double)m - mx[0]);
-    }
+#pragma unroll
+    for (int s = 0; s < K; ++s)
+      if (pm[s] != -INFINITY) S += ps[s] * exp((double)pm[s] - mx[0]);
     S = block_sum(S, red);
     lse = mx[0] + log(S);
   }
   bool fallback = false;
-  if constexpr (MODE == kSelResidual) fallback = !(block_sum(wsum, red) > 0.0);
+  if constexpr (kResid) fallback = !(block_sum(wsum, red) > 0.0);
 
+  const int tj = tid >> 3, tp = tid & 7;
   int bstar = -1;
   for (int attempt = 0; attempt < 2 && bstar < 0; ++attempt) {
     if (attempt == 1) {
-      if (MODE != kSelResidual || fallback) break;
+      if (!kResid || fallback) break;
       fallback = true;  // no block of the residual has binary64 mass: p^t instead
     }
-    const BlockCands C = (MODE == kSelResidual && fallback) ? a.cand_f : a.cand;
-    const double Ls = (MODE == kSelResidual && fallback) ? mx[2] : mx[1];
-    // 2. blocks whose upper bound reaches the largest lower bound
+    const bool useF = kResid && fallback;
+    const double Ls = useF ? mx[2] : mx[1];
+    // 3. blocks whose upper bound reaches the largest lower bound
     if (tid == 0) {
-      ncand = 0;
-      overflow = 0;
+      sh.ncand = 0;
+      sh.overflow = 0;
     }
     __syncthreads();
-    for (int j = tid; j < a.nsplit; j += nt) {
-      const double h1 = ld<COH>(C.hi1 + rec0 + j), h2 = ld<COH>(C.hi2 + rec0 + j);
-      const int b1 = ld<COH>(C.b1 + rec0 + j);
-      if (h2 > -INFINITY && h2 >= Ls) {
+#pragma unroll
+    for (int s = 0; s < K; ++s) {
+      const int j = tid + s * nt;
+      const double hh1 = useF ? h1f[s] : h1[s];
+      const double hh2 = useF ? h2f[s] : h2[s];
+      const int bb1 = useF ? b1f[s] : b1[s];
+      if (j < a.nsplit && hh2 > -INFINITY && hh2 >= Ls) {
         const int t0 = split_tile(j, a.nsplit, a.ntiles, a.tiles_per_stage);
         const int t1 = split_tile(j + 1, a.nsplit, a.ntiles, a.tiles_per_stage);
-        const int pos = atomicAdd(&ncand, t1 - t0);
+        const int pos = atomicAdd(&sh.ncand, t1 - t0);
         if (pos + (t1 - t0) <= kMaxCand) {
-          for (int t = t0; t < t1; ++t) cand[pos + t - t0] = t;
+          for (int t = t0; t < t1; ++t) sh.cand[pos + t - t0] = t;
         } else {
-          overflow = 1;
+          sh.overflow = 1;
         }
-      } else if (h1 > -INFINITY && h1 >= Ls && b1 >= 0) {
-        const int pos = atomicAdd(&ncand, 1);
-        if (pos < kMaxCand) cand[pos] = b1;
-        else overflow = 1;
+      } else if (j < a.nsplit && hh1 > -INFINITY && hh1 >= Ls && bb1 >= 0) {
+        const int pos = atomicAdd(&sh.ncand, 1);
+        if (pos < kMaxCand) sh.cand[pos] = bb1;
+        else sh.overflow = 1;
       }
     }
     __syncthreads();
-    const bool all = overflow != 0;
-    const int total = all ? a.ntiles : min(ncand, kMaxCand);
-    // 3. binary64 score of each such block: 8 threads per token for the bias,
-    //    then one wave takes the block's log-mass and Gumbel variate
-    const int tj = tid >> 3, tp = tid & 7;
+    const bool all = sh.overflow != 0;
+    const int total = all ? a.ntiles : min(sh.ncand, kMaxCand);
+    // 4. binary64 score of each such block: eight threads per token for the
+    //    bias; the token's stored logits, W2 chunks and member Gumbel variate
+    //    are fetched and computed together, then one wave takes the block's
+    //    log-mass and Gumbel variate
     double best = -INFINITY;
     int bb = -1;
     for (int ci = 0; ci < total; ++ci) {
-      const int blk = all ? ci : cand[ci];
+      const int blk = all ? ci : sh.cand[ci];
       const int v = blk * kTile + tj;
-      double part = 0.0;
-      if (kBias && tid < 256 && v < a.V) part = bias64_part(a.W2p, bf16, w1s, v, tp);
+      const bool tok = tid < 256 && v < a.V;
+      BiasLoad L;
+      if (kBias && tok) bias64_load(L, a.W2p, bf16, v, tp);
+      double u = 0.0, t = 0.0;
+      if (tok && tp == 0) {
+        if constexpr (MODE != kSelBonus) u = stored(a.U, bf16, q.uoff + v);
+        if constexpr (MODE != kSelDraft) t = stored(a.T, bf16, q.toff + v);
+      }
+      const double g = (tok && tp == 1) ? gumbel_at(a.seed, sblock + kMemberStream, q.r, q.k, (uint32_t)v) : 0.0;
+      double part = (kBias && tok) ? bias64_dot(L, bf16, w1s, tp) : 0.0;
       part += __shfl_xor(part, 1, 64);
       part += __shfl_xor(part, 2, 64);
       part += __shfl_xor(part, 4, 64);
-      if (tid < 256 && tp == 0) zc[tj] = v < a.V ? log_weight<MODE>(a, bf16, fallback, q, part, v) : -INFINITY;
+      if (tid < 256 && tp == 0) sh.zc[tj] = tok ? log_weight<MODE>(fallback, q, u, t, part) : -INFINITY;
+      if (tid < 256 && tp == 1) sh.gc[tj] = g;
       __syncthreads();
       if (tid < 32) {
-        const double w = zc[tid];
+        const double w = sh.zc[tid];
         double m = w;
 #pragma unroll
         for (int off = 1; off < 32; off <<= 1) m = fmax(m, __shfl_xor(m, off, 64));
@@ -289,27 +348,27 @@ __device__ void select_row(const SelectArgs& a, int bf16_flag, int i, SelShared&
           if (bb < 0 || sc > best || (sc == best && blk < bb)) {
             best = sc;
             bb = blk;
-            zb[tid] = w;
+            sh.zb[tid] = w;
+            sh.gb[tid] = sh.gc[tid];
           }
         }
       }
       __syncthreads();
     }
-    if (tid == 0) bstar_sh = bb;
+    if (tid == 0) sh.bstar = bb;
     __syncthreads();
-    bstar = bstar_sh;
+    bstar = sh.bstar;
     __syncthreads();
   }
 
-  // 4. member of the winning block (its log-weights are in zb)
+  // 5. member of the winning block (its log-weights and variates are in zb, gb)
   if (tid < 32) {
     int x = -1;
     double wx = -INFINITY;
     if (bstar >= 0) {
       const int v = bstar * kTile + tid;
-      const double w = zb[tid];
-      const double sc = (w > -INFINITY) ? w + gumbel_at(a.seed, sblock + kMemberStream, q.r, q.k, (uint32_t)v)
-                                        : -INFINITY;
+      const double w = sh.zb[tid];
+      const double sc = (w > -INFINITY) ? w + sh.gb[tid] : -INFINITY;
       double bsc = sc;
       int bv = sc > -INFINITY ? v : -1;
 #pragma unroll
@@ -325,7 +384,7 @@ __device__ void select_row(const SelectArgs& a, int bf16_flag, int i, SelShared&
       wx = __shfl(w, x >= 0 ? x - bstar * kTile : 0, 64);
     }
     if (tid == 0) {
-      if constexpr (MODE == kSelDraft) {
+      if constexpr (kDraft) {
         const int64_t o = (int64_t)q.r * a.gamma + (q.k - 1);
         st<COH>(a.out_tokens + o, x);
         a.out_lse[o] = lse;
