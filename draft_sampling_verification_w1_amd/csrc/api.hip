@@ -83,7 +83,7 @@ BlockCands cands_at(void* ws, const CandLayout& L);
 
 struct DraftLayout {
   BiasGeometry g;
-  size_t pm, ps, bytes;
+  size_t pm, ps, bop, bytes;
   CandLayout cand;
 };
 
@@ -95,6 +95,8 @@ DraftLayout draft_layout(const dspark_problem* p) {
   L.pm = c.take(n * sizeof(float));
   L.ps = c.take(n * sizeof(double));
   L.cand = take_cands(c, n);
+  // B operands of every row a bias workgroup covers (whole blocks of rows)
+  L.bop = c.take((size_t)L.g.row_blocks * L.g.rows_per_block * kRank * 2);
   L.bytes = c.off;
   return L;
 }
@@ -363,9 +365,14 @@ __attribute__((visibility("default"))) int dspark_draft_step(
   q.out_tokens = tokens;
   q.out_lse = lse;
   q.out_logq = logq;
+  // bf16: each select writes the drafted tokens' W1 rows as the next
+  // position's matrix-core operands; the first position gathers the anchors'
+  void* bop = bf16 ? at<void>(ws, L.bop) : nullptr;
   for (int k = 1; k <= p->gamma; ++k) {
     a.k = k;
     q.k = k;
+    a.bop = k > 1 ? bop : nullptr;
+    q.bop_out = k < p->gamma ? bop : nullptr;
     hipError_t e = launch_bias_pass(kModeDraft, bf16, a, s);
     if (e != hipSuccess) return hip_fail(e, "draft pass");
     e = launch_select(kSelDraft, bf16, q, s);

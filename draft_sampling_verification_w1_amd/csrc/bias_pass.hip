@@ -67,7 +67,7 @@ struct RowCtx {
 
 template <bool COH = false>
 __device__ __forceinline__ RowCtx row_ctx(const BiasPassArgs& a, int i, int active_rows, bool bf16,
-                                          int kpos) {
+                                          int kpos, bool need_prev = true) {
   RowCtx c;
   c.active = i < active_rows;
   c.r = 0;
@@ -86,11 +86,13 @@ __device__ __forceinline__ RowCtx row_ctx(const BiasPassArgs& a, int i, int acti
     c.r = i;
     c.k = kpos;
   }
-  const int32_t* tp = a.tokens + (int64_t)c.r * a.gamma + (c.k - 2);
-  int x = (c.k == 1) ? a.anchors[c.r]
-                     : (COH ? __hip_atomic_load(const_cast<int32_t*>(tp), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
-                            : *tp);
-  c.prev = min(max(x, 0), a.V - 1);
+  if (need_prev) {
+    const int32_t* tp = a.tokens + (int64_t)c.r * a.gamma + (c.k - 2);
+    int x = (c.k == 1) ? a.anchors[c.r]
+                       : (COH ? __hip_atomic_load(const_cast<int32_t*>(tp), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                              : *tp);
+    c.prev = min(max(x, 0), a.V - 1);
+  }
   const size_t esz = bf16 ? 2 : 4;
   c.urow = (const char*)a.U + ((int64_t)c.r * a.gamma + (c.k - 1)) * (int64_t)a.V * esz;
   if (a.T) c.trow = (const char*)a.T + ((int64_t)c.r * (a.gamma + 1) + (c.k - 1)) * (int64_t)a.V * esz;
@@ -314,7 +316,10 @@ __device__ void bias_body(const BiasPassArgs& a, int split, int row_block, int k
   const int c_end = (t_end + ST - 1) / ST;
 
   const int row = row0 + wave * 32 + n;
-  const RowCtx rc = row_ctx<COH>(a, row, active_rows, true, kpos);
+  // the draft's B operands come ready-made from the previous position's select
+  // (a.bop), except at the first position
+  const bool bop_ready = MODE == kModeDraft && a.bop != nullptr;
+  const RowCtx rc = row_ctx<COH>(a, row, active_rows, true, kpos, !bop_ready);
   LaneState<MODE> st;
   st.init();
 
@@ -382,7 +387,14 @@ __device__ void bias_body(const BiasPassArgs& a, int split, int row_block, int k
   // the W1 rows (otherwise every tile drains the prefetch).
   load_stage(0, c_begin);
   bf16x8 bop[kSteps];
-  {
+  if (bop_ready) {
+    const u32x4* src = reinterpret_cast<const u32x4*>(a.bop) + bop_chunk(row, 0, h);
+#pragma unroll
+    for (int s = 0; s < kSteps; ++s) {
+      const u32x4 v = src[s * 64];
+      bop[s] = as_bf16x8(rc.active ? v : (u32x4){0u, 0u, 0u, 0u});
+    }
+  } else {
     const u32x4* w1 = reinterpret_cast<const u32x4*>(
         reinterpret_cast<const uint16_t*>(a.W1) + (int64_t)rc.prev * kRank + 128 * h);
 #pragma unroll

@@ -40,6 +40,15 @@ struct BlockCands {
 // Arguments of one split-vocabulary pass over a set of (request, position)
 // rows: bias B = W1[x_{k-1}] W2 plus backbone logits U, consumed by a
 // mode-specific epilogue.  Partial records are indexed [row * nsplit + split].
+// Matrix-core B operands of the draft: the W1 row of row r's previous token,
+// bf16, in the lane order of the bias pass (16-byte chunk c = 16h + s of the
+// row, elements [128h + 8s, 128h + 8s + 8), goes to lane (r % 32) + 32h of
+// step s of 32-row group r / 32), so that a wave loads its 32 rows' operands
+// with 16 lane-contiguous 1 KB loads.  Index of that chunk, in 16-byte units:
+__host__ __device__ inline int64_t bop_chunk(int r, int s, int h) {
+  return ((int64_t)(r >> 5) * kSteps + s) * 64 + (r & 31) + 32 * h;
+}
+
 struct BiasPassArgs {
   int R, gamma, V;
   uint64_t seed;
@@ -53,6 +62,7 @@ struct BiasPassArgs {
   const void* W2p;
   const int32_t* anchors;
   const int32_t* tokens;
+  const void* bop;            // draft, bf16: B operands (bop_chunk order), or null: gather W1 rows
   const double* lse_d;        // [R*gamma]
   const double* lse_t;        // [R*(gamma+1)]
   int ntiles;                 // ceil(V / 32)
@@ -108,6 +118,7 @@ struct SelectArgs {
   BlockCands cand;
   BlockCands cand_f;
   const float* wpos;
+  void* bop_out;              // draft, bf16: B operands for the next position (bop_chunk order) or null
   int32_t* out_tokens;        // draft: tokens [R, gamma]; residual / bonus: out_token [R]
   double* out_lse;            // draft
   double* out_logq;           // draft

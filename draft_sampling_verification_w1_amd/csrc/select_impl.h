@@ -167,7 +167,8 @@ struct SelShared {
   int ncand, overflow;
   double zc[32], gc[32];  // scored block: log-weights and member Gumbel variates
   double zb[32], gb[32];  // best block so far
-  int bstar;
+  int bstar, brun;        // winning block; best block after the latest scoring
+  u32x4 rows[32 * 32];    // draft: W1 rows of the best block's tokens (16-byte chunks)
 };
 
 // The draw of row i (draft: request i at position a.k; residual / bonus: entry
@@ -272,6 +273,10 @@ __device__ void select_row(const SelectArgs& a, int bf16_flag, int i, SelShared&
   if constexpr (kResid) fallback = !(block_sum(wsum, red) > 0.0);
 
   const int tj = tid >> 3, tp = tid & 7;
+  // draft: the W1 rows of a scored block's tokens are fetched with it, so that
+  // the drafted token's row can be written out as the next position's B
+  // operand without another round trip
+  const bool pre_rows = kDraft && a.bop_out != nullptr;
   int bstar = -1;
   for (int attempt = 0; attempt < 2 && bstar < 0; ++attempt) {
     if (attempt == 1) {
@@ -322,6 +327,12 @@ __device__ void select_row(const SelectArgs& a, int bf16_flag, int i, SelShared&
       const bool tok = tid < 256 && v < a.V;
       BiasLoad L;
       if (kBias && tok) bias64_load(L, a.W2p, bf16, v, tp);
+      u32x4 wrow[4];
+      if (pre_rows && tok) {
+        const u32x4* src = reinterpret_cast<const u32x4*>(a.W1) + (int64_t)v * (kRank / 8) + 4 * tp;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) wrow[c] = src[c];
+      }
       double u = 0.0, t = 0.0;
       if (tok && tp == 0) {
         if constexpr (MODE != kSelBonus) u = stored(a.U, bf16, q.uoff + v);
@@ -352,8 +363,13 @@ __device__ void select_row(const SelectArgs& a, int bf16_flag, int i, SelShared&
             sh.gb[tid] = sh.gc[tid];
           }
         }
+        if (tid == 0) sh.brun = bb;
       }
       __syncthreads();
+      if (pre_rows && tok && sh.brun == blk) {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) sh.rows[tj * 32 + 4 * tp + c] = wrow[c];
+      }
     }
     if (tid == 0) sh.bstar = bb;
     __syncthreads();
@@ -382,6 +398,14 @@ __device__ void select_row(const SelectArgs& a, int bf16_flag, int i, SelShared&
       }
       x = bv;
       wx = __shfl(w, x >= 0 ? x - bstar * kTile : 0, 64);
+    }
+    if (pre_rows) {
+      // lane c writes chunk c of the row of max(x, 0) (the next pass clamps
+      // the previous token the same way)
+      const int c = tid;
+      const u32x4 val = x >= 0 ? sh.rows[(x - bstar * kTile) * 32 + c]
+                               : reinterpret_cast<const u32x4*>(a.W1)[c];
+      reinterpret_cast<u32x4*>(a.bop_out)[bop_chunk(q.r, c & 15, c >> 4)] = val;
     }
     if (tid == 0) {
       if constexpr (kDraft) {
