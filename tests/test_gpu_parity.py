@@ -175,3 +175,39 @@ def test_schedule_against_oracle(dev, R, gamma):
         gs = dev.schedule(to_dev(c), to_dev(sps))
         torch.cuda.synchronize()
         compare_schedule(os_, gs["a"].cpu().numpy(), {k: v.cpu().numpy() for k, v in gs.items() if k != "a"})
+
+
+def test_schedule_factor_above_one(dev):
+    """A factor just above 1 (a c* rounded up past 1, say) makes a request's
+    products rise by an ulp, so its positions are no longer in key order.  The
+    kernel must still take the candidates in the order of the key (-a, r, j):
+    the products, the Theta path and the stopping point are compared with the
+    oracle, and each length with the largest selected position of its request
+    (where the set is not a prefix, the oracle's Algorithm 1 keeps the last
+    one it visits instead)."""
+    import torch
+    from oracle import oracle as O
+    from draft_sampling_verification_w1_amd import synth
+    R, gamma = 64, 16
+    cfg = synth.scaled(synth.CONFIGS["full_round"], name="sched_up", R=R, gamma=gamma, n_sps=R * (gamma + 1))
+    rng = np.random.default_rng(11)
+    c = rng.uniform(0.55, 0.95, (R, gamma)).astype(np.float32)
+    up = rng.random((R, gamma)) < 0.25
+    up[:, 0] = False
+    c[up] = np.float32(1.0) + np.float32(2.0 ** -23)
+    a = O.prefix_products(c)
+    assert (np.diff(a, axis=1) > 0).any(), "no rising product: the case is not exercised"
+    sps = synth.sps_table(cfg)
+    os_ = O.schedule(a, sps)
+    gs = dev.schedule(to_dev(c), to_dev(sps))
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(gs["a"].cpu().numpy(), a)
+    np.testing.assert_array_equal(gs["stats"].cpu().numpy(), os_["stats"])
+    np.testing.assert_array_equal(gs["theta_path"].cpu().numpy(), os_["theta_path"])
+    # largest selected position per request, from the key order
+    order = np.lexsort((np.tile(np.arange(gamma), R), np.repeat(np.arange(R), gamma), -a.ravel()))
+    n_sel = int(os_["stats"][3])
+    want = np.zeros(R, np.int32)
+    for o in order[:n_sel]:
+        want[o // gamma] = max(want[o // gamma], o % gamma + 1)
+    np.testing.assert_array_equal(gs["lengths"].cpu().numpy(), want)
