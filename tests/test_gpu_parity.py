@@ -44,7 +44,9 @@ def _run_case(dspark, cfg, lengths=None, check_schedule=True):
     torch.cuda.synchronize()
     gn = {k: (v.cpu().numpy() if v is not None else None) for k, v in g.items()}
     n, ties = compare_verify(ov, gn)
-    log(f"  verify: {n} requests compared, {ties} near-ties; mean c* {np.nanmean(ov['cstar']):.4f}, "
+    fin = ov["cstar"][~np.isnan(ov["cstar"])]
+    mean_c = f"{fin.mean():.4f}" if fin.size else "none verified"
+    log(f"  verify: {n} requests compared, {ties} near-ties; mean c* {mean_c}, "
         f"mean accepted {ov['n_accept'].mean():.3f}")
 
     if check_schedule:
@@ -211,3 +213,86 @@ def test_schedule_factor_above_one(dev):
     for o in order[:n_sel]:
         want[o // gamma] = max(want[o // gamma], o % gamma + 1)
     np.testing.assert_array_equal(gs["lengths"].cpu().numpy(), want)
+
+
+def test_single_token_vocabulary(dev):
+    """V = 1: every draw is token 0, every c* is 1 and every position is accepted."""
+    from draft_sampling_verification_w1_amd import synth
+    cfg = synth.scaled(synth.CONFIGS["qwen3_4b"], name="v1", R=3, gamma=2, V=1, n_sps=3 * 3)
+    _run_case(dev, cfg)
+
+
+def test_largest_block(dev):
+    """gamma = 64, the largest block the library accepts."""
+    from draft_sampling_verification_w1_amd import synth
+    cfg = synth.scaled(synth.CONFIGS["qwen3_4b"], name="g64", R=2, gamma=64, V=300, n_sps=2 * 65)
+    _run_case(dev, cfg)
+
+
+def test_empty_verification(dev):
+    """Every verify length 0: no position is checked, every request gets the
+    bonus draw from its first target row, c* is NaN throughout."""
+    from draft_sampling_verification_w1_amd import synth
+    cfg = synth.scaled(synth.CONFIGS["high_concurrency"], name="len0", R=9, gamma=3, V=2000, n_sps=9 * 4)
+    _run_case(dev, cfg, lengths=np.zeros(9, np.int32), check_schedule=False)
+
+
+def test_round_replayed_from_graph(dev):
+    """The whole round (draft, verify of every position, schedule on c*)
+    captured once in a graph and replayed: each replay reproduces the eager
+    round, with an eager round on other inputs run between replays over the
+    same buffers (the library allocates nothing, sets no memory with memset
+    and waits on nothing inside a call)."""
+    import torch
+    from draft_sampling_verification_w1_amd import synth
+    R, gamma, V, seed = 40, 4, 5000, 123
+    cfg = synth.scaled(synth.CONFIGS["qwen3_4b"], name="graph", R=R, gamma=gamma, V=V, n_sps=R * (gamma + 1))
+    inp = gen_inputs(cfg)
+    U, W1, A = to_dev(inp["U"]), to_dev(inp["W1"]), to_dev(inp["anchors"])
+    W2p = dev.pack_w2(to_dev(inp["W2"]), V)
+    rng = np.random.default_rng(4)
+    Tn = np.concatenate([O_u(inp["U"]), O_u(inp["U"])[:, :1]], axis=1)
+    Tn = Tn + rng.standard_normal(Tn.shape).astype(np.float32)
+    T = to_dev(synth.f32_to_bf16_bits(Tn))
+    sps = to_dev(synth.sps_table(cfg))
+    ws = dev.workspace(dev.problem(R, gamma, V, torch.bfloat16, seed))
+    d_out = dev.draft_step(U, W1, W2p, A, seed, ws=ws)
+    v_out = dev.verify(U, W1, W2p, A, *d_out, T, None, seed, ws=ws)
+    s_out = dev.schedule(v_out["cstar"], sps)
+
+    def round_(s):
+        dev.draft_step(U, W1, W2p, A, s, ws=ws, out=d_out)
+        dev.verify(U, W1, W2p, A, *d_out, T, None, s, ws=ws, out=v_out)
+        dev.schedule(v_out["cstar"], sps, out=s_out)
+
+    def snapshot():
+        torch.cuda.synchronize()
+        return [t.clone() for t in d_out] + [v.clone() for v in v_out.values() if v is not None] + \
+               [v.clone() for v in s_out.values() if v is not None]
+
+    round_(seed)
+    ref = snapshot()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        round_(seed)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        round_(seed)
+    for rep in range(3):
+        round_(seed + 1 + rep)  # eager work over the same buffers
+        torch.cuda.synchronize()
+        g.replay()
+        got = snapshot()
+        for x, y in zip(got, ref):
+            assert torch.equal(x.nan_to_num(nan=-7.0), y.nan_to_num(nan=-7.0)) if x.is_floating_point() \
+                else torch.equal(x, y), f"replay {rep} differs from the eager round"
+    log(f"  graph: 3 replays equal the eager round")
+
+
+def O_u(U):
+    """bf16 bits [R, gamma, V] -> float32 values (test input construction)."""
+    from draft_sampling_verification_w1_amd import synth
+    return synth.bf16_bits_to_f32(U)
