@@ -65,7 +65,6 @@ struct RowCtx {
   float eps;       // residual: relative error bound of the binary32 p^d, p^t
 };
 
-template <bool COH = false>
 __device__ __forceinline__ RowCtx row_ctx(const BiasPassArgs& a, int i, int active_rows, bool bf16,
                                           int kpos, bool need_prev = true) {
   RowCtx c;
@@ -88,9 +87,7 @@ __device__ __forceinline__ RowCtx row_ctx(const BiasPassArgs& a, int i, int acti
   }
   if (need_prev) {
     const int32_t* tp = a.tokens + (int64_t)c.r * a.gamma + (c.k - 2);
-    int x = (c.k == 1) ? a.anchors[c.r]
-                       : (COH ? __hip_atomic_load(const_cast<int32_t*>(tp), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
-                              : *tp);
+    const int x = (c.k == 1) ? a.anchors[c.r] : *tp;
     c.prev = min(max(x, 0), a.V - 1);
   }
   const size_t esz = bf16 ? 2 : 4;
@@ -256,24 +253,24 @@ __device__ __forceinline__ void epilogue(LaneState<MODE>& st, const float* z, co
 
 // Partial record of the split for the lane's row, written by the lower half of
 // the wave (both halves hold the same row; the c* sums are per half).
-template <int MODE, bool COH = false>
+template <int MODE>
 __device__ __forceinline__ void finish(const LaneState<MODE>& st, const RowCtx& rc, int row,
                                        int split, const BiasPassArgs& a, bool writer) {
   const int64_t o = (int64_t)row * a.nsplit + split;
   if constexpr (MODE == kModeDraft) {
     if (writer && rc.active) {
-      store_to<COH>(a.pm + o, st.M);
-      store_to<COH>(a.ps + o, st.S);
-      st.cand.template store<COH>(a.cand, o);
+      a.pm[o] = st.M;
+      a.ps[o] = st.S;
+      st.cand.store(a.cand, o);
     }
   } else if constexpr (MODE == kModeCstar) {
     const double s = st.s + xor32(st.s);
-    if (writer && rc.active) store_to<COH>(a.ps + o, s);
+    if (writer && rc.active) a.ps[o] = s;
   } else {
     if (writer && rc.active) {
-      st.cand.template store<COH>(a.cand, o);
-      st.candf.template store<COH>(a.cand_f, o);
-      store_to<COH>(a.wpos + o, st.wpos);
+      st.cand.store(a.cand, o);
+      st.candf.store(a.cand_f, o);
+      a.wpos[o] = st.wpos;
     }
   }
 }
@@ -287,9 +284,8 @@ __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast
 // tiles to a double-buffered workgroup area, the row segments to the wave's
 // own area (xor-swizzled 16-byte slots); one barrier per stage publishes the
 // W2 tiles.  VEC: rows 16-byte aligned (vector loads), else scalar loads.
-// One (split, row block) of a pass.  COH: the drafted tokens were written and
-// the records are read by other workgroups of the same kernel.
-template <int MODE, int D, bool VEC, bool COH>
+// One (split, row block) of a pass.
+template <int MODE, int D, bool VEC>
 __device__ void bias_body(const BiasPassArgs& a, int split, int row_block, int kpos) {
   constexpr bool kNeedT = MODE != kModeDraft;
   constexpr int ST = 2;
@@ -319,7 +315,7 @@ __device__ void bias_body(const BiasPassArgs& a, int split, int row_block, int k
   // the draft's B operands come ready-made from the previous position's select
   // (a.bop), except at the first position
   const bool bop_ready = MODE == kModeDraft && a.bop != nullptr;
-  const RowCtx rc = row_ctx<COH>(a, row, active_rows, true, kpos, !bop_ready);
+  const RowCtx rc = row_ctx(a, row, active_rows, true, kpos, !bop_ready);
   LaneState<MODE> st;
   st.init();
 
@@ -460,12 +456,12 @@ __device__ void bias_body(const BiasPassArgs& a, int split, int row_block, int k
       }
     }
   }
-  finish<MODE, COH>(st, rc, row, split, a, h == 0);
+  finish<MODE>(st, rc, row, split, a, h == 0);
 }
 
 template <int MODE, int D, bool VEC>
 __global__ __launch_bounds__(kThreads) void k_bias_bf16(const BiasPassArgs a) {
-  bias_body<MODE, D, VEC, false>(a, blockIdx.x, blockIdx.y, a.k);
+  bias_body<MODE, D, VEC>(a, blockIdx.x, blockIdx.y, a.k);
 }
 
 // Binary32 rows: same row/lane layout, bias by VALU dot products against the

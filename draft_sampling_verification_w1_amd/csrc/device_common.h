@@ -218,15 +218,6 @@ __device__ __forceinline__ float sum_halves(float x) {
 // Partial records written per (vocabulary split, row) and merged later.
 // Arrays are structure-of-arrays with row stride `ld` (the row capacity).
 // ---------------------------------------------------------------------------
-// Store that other workgroups of the same kernel can read after a grid-wide
-// barrier (COH): a device-scope relaxed atomic store, which is not held in the
-// writer's per-XCD L2.
-template <bool COH, typename T>
-__device__ __forceinline__ void store_to(T* p, T v) {
-  if constexpr (COH) __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  else *p = v;
-}
-
 // Running block-candidate record of a split (see BlockCands).
 struct CandState {
   float lo, hi1, hi2;
@@ -256,12 +247,11 @@ struct CandState {
       hi2 = fmaxf(hi2, o.hi1);
     }
   }
-  template <bool COH = false>
   __device__ void store(const BlockCands& c, int64_t o) const {
-    store_to<COH>(c.lo + o, lo);
-    store_to<COH>(c.hi1 + o, hi1);
-    store_to<COH>(c.b1 + o, b1);
-    store_to<COH>(c.hi2 + o, hi2);
+    c.lo[o] = lo;
+    c.hi1[o] = hi1;
+    c.b1[o] = b1;
+    c.hi2[o] = hi2;
   }
 };
 

@@ -25,7 +25,7 @@ namespace {
 template <int MODE>
 __global__ __launch_bounds__(256) void k_select(const SelectArgs a, int bf16_flag) {
   __shared__ sel::SelShared sh;
-  sel::select_row<MODE, false>(a, bf16_flag, blockIdx.x, sh, a.k);
+  sel::select_row<MODE>(a, bf16_flag, blockIdx.x, sh, a.k);
 }
 
 }  // namespace

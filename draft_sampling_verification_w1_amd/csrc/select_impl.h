@@ -67,19 +67,6 @@ __device__ __forceinline__ double bias64_dot(const BiasLoad& L, bool bf16, const
   return acc;
 }
 
-// COH: loads of data written by other workgroups of the same kernel, which
-// must bypass the non-coherent per-XCD L2 (device-scope relaxed atomics).
-template <bool COH, typename T>
-__device__ __forceinline__ T ld(const T* p) {
-  if constexpr (COH) return __hip_atomic_load(const_cast<T*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  else return *p;
-}
-template <bool COH, typename T>
-__device__ __forceinline__ void st(T* p, T v) {
-  if constexpr (COH) __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  else *p = v;
-}
-
 __device__ __forceinline__ double stored(const void* p, bool bf16, int64_t i) {
   return bf16 ? (double)bf16_at(reinterpret_cast<const uint16_t*>(p), i)
               : (double)reinterpret_cast<const float*>(p)[i];
@@ -172,9 +159,8 @@ struct SelShared {
 };
 
 // The draw of row i (draft: request i at position a.k; residual / bonus: entry
-// i of the work list).  blockDim.x = 256; COH: split records and drafted tokens
-// were written by other workgroups of the same kernel.
-template <int MODE, bool COH>
+// i of the work list).  blockDim.x = 256.
+template <int MODE>
 __device__ void select_row(const SelectArgs& a, int bf16_flag, int i, SelShared& sh, int kpos) {
   constexpr int K = RecSlots<MODE>::K;
   constexpr bool kDraft = MODE == kSelDraft;
@@ -210,7 +196,7 @@ __device__ void select_row(const SelectArgs& a, int bf16_flag, int i, SelShared&
     }
   }
   if constexpr (kBias) {
-    const int x = (q.k == 1) ? a.anchors[q.r] : ld<COH>(a.tokens + (int64_t)q.r * a.gamma + (q.k - 2));
+    const int x = (q.k == 1) ? a.anchors[q.r] : a.tokens[(int64_t)q.r * a.gamma + (q.k - 2)];
     q.prev = min(max(x, 0), a.V - 1);
     q.uoff = ((int64_t)q.r * a.gamma + (q.k - 1)) * a.V;
     if (tid < kRank) w1s[tid] = stored(a.W1, bf16, (int64_t)q.prev * kRank + tid);
@@ -232,20 +218,20 @@ __device__ void select_row(const SelectArgs& a, int bf16_flag, int i, SelShared&
     ps[s] = 0.0;
     b1[s] = b1f[s] = -1;
     if (has) {
-      lo[s] = ld<COH>(a.cand.lo + o);
-      h1[s] = ld<COH>(a.cand.hi1 + o);
-      h2[s] = ld<COH>(a.cand.hi2 + o);
-      b1[s] = ld<COH>(a.cand.b1 + o);
+      lo[s] = a.cand.lo[o];
+      h1[s] = a.cand.hi1[o];
+      h2[s] = a.cand.hi2[o];
+      b1[s] = a.cand.b1[o];
       if constexpr (kDraft) {
-        pm[s] = ld<COH>(a.pm + o);
-        ps[s] = ld<COH>(a.ps + o);
+        pm[s] = a.pm[o];
+        ps[s] = a.ps[o];
       }
       if constexpr (kResid) {
-        lof[s] = ld<COH>(a.cand_f.lo + o);
-        h1f[s] = ld<COH>(a.cand_f.hi1 + o);
-        h2f[s] = ld<COH>(a.cand_f.hi2 + o);
-        b1f[s] = ld<COH>(a.cand_f.b1 + o);
-        wsum += (double)ld<COH>(a.wpos + o);
+        lof[s] = a.cand_f.lo[o];
+        h1f[s] = a.cand_f.hi1[o];
+        h2f[s] = a.cand_f.hi2[o];
+        b1f[s] = a.cand_f.b1[o];
+        wsum += (double)a.wpos[o];
       }
     }
   }
@@ -410,7 +396,7 @@ __device__ void select_row(const SelectArgs& a, int bf16_flag, int i, SelShared&
     if (tid == 0) {
       if constexpr (kDraft) {
         const int64_t o = (int64_t)q.r * a.gamma + (q.k - 1);
-        st<COH>(a.out_tokens + o, x);
+        a.out_tokens[o] = x;
         a.out_lse[o] = lse;
         a.out_logq[o] = wx - lse;
       } else {
