@@ -146,16 +146,25 @@ __global__ __launch_bounds__(256) void k_decide(int R, int gamma, int V, uint64_
                                                 int32_t* n_accept, uint8_t* accept_mask,
                                                 double* lse_t_out) {
   __shared__ double lse_k[64];
+  __shared__ uint8_t ok_k[64];
   const int r = blockIdx.x;
   const int L = w.req_len[r];
   const int off = w.req_off[r];
-  for (int k = 1; k <= L; ++k) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  // 1. lse of each verified target row: wave q merges the split partials of
+  //    positions q + 1, q + 5, ... (no workgroup barrier per position)
+  for (int k = wave + 1; k <= L; k += 4) {
     const int64_t base = (int64_t)(off + k - 1) * w.ns_t;
     float m = -INFINITY;
     double s = 0.0;
-    for (int j = threadIdx.x; j < w.ns_t; j += 256) lse_merge(m, s, w.lt_m[base + j], w.lt_s[base + j]);
-    block_lse(m, s);
-    if (threadIdx.x == 0) lse_k[k - 1] = (double)m + log(s);
+    for (int j = lane; j < w.ns_t; j += 64) lse_merge(m, s, w.lt_m[base + j], w.lt_s[base + j]);
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const float m2 = __shfl_xor(m, o, 64);
+      const double s2 = __shfl_xor(s, o, 64);
+      lse_merge(m, s, m2, s2);
+    }
+    if (lane == 0) lse_k[k - 1] = (double)m + log(s);
   }
   __syncthreads();
   for (int k = threadIdx.x + 1; k <= gamma + 1; k += 256) {
@@ -163,20 +172,24 @@ __global__ __launch_bounds__(256) void k_decide(int R, int gamma, int V, uint64_
     w.lse_t[(int64_t)r * (gamma + 1) + (k - 1)] = v;
     if (lse_t_out) lse_t_out[(int64_t)r * (gamma + 1) + (k - 1)] = v;
   }
+  // 2. every verified position's test at once: accept x_k iff ln u < ln p^t(x_k) - ln p^d(x_k)
+  for (int k = threadIdx.x + 1; k <= L; k += 256) {
+    const int64_t o = (int64_t)r * gamma + (k - 1);
+    const int x = min(max(tokens[o], 0), V - 1);
+    const double tx = (double)elem_at(T, ((int64_t)r * (gamma + 1) + (k - 1)) * (int64_t)V + x);
+    const double rho = (tx - lse_k[k - 1]) - logq[o];
+    const uint32_t wd = noise_block(seed, kStreamAccept, r, k, 0).x;
+    ok_k[k - 1] = log(uniform_f64(wd)) < rho ? 1 : 0;
+  }
+  __syncthreads();
+  // 3. the first rejection ends the accepted prefix
   if (threadIdx.x == 0) {
     int n = L, kstar = 0;
     for (int k = 1; k <= gamma; ++k) {
       uint8_t mk = 255;
       if (k <= L && kstar == 0) {
-        const int64_t o = (int64_t)r * gamma + (k - 1);
-        const int x = min(max(tokens[o], 0), V - 1);
-        const double tx = (double)elem_at(T, ((int64_t)r * (gamma + 1) + (k - 1)) * (int64_t)V + x);
-        const double rho = (tx - lse_k[k - 1]) - logq[o];
-        const uint32_t wd = noise_block(seed, kStreamAccept, r, k, 0).x;
-        const double ln_u = log(uniform_f64(wd));
-        const bool ok = ln_u < rho;
-        mk = ok ? 1 : 0;
-        if (!ok) {
+        mk = ok_k[k - 1];
+        if (!mk) {
           kstar = k;
           n = k - 1;
         }
