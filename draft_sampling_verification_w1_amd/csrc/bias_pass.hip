@@ -351,14 +351,15 @@ __device__ void bias_body(const BiasPassArgs& a, int split, int row_block, int k
   auto load_stage = [&](int d, int c) {
     const bool live = c < c_end;
     const int t0 = c * ST;
-    // W2 chunks come from the clamped tile on every stage: a padding stage's
-    // copy is never read, and a load that depended on `live` would let the
-    // compiler fold the constant source and drop loads on that path, which
-    // breaks its exact count of loads in flight (it then over-waits).
+    // W2 chunks are loaded on every stage, tiles past the split clamped to its
+    // last tile (already in L2; the copy is never read).  A load that depended
+    // on `live` would let the compiler fold a constant source and drop loads on
+    // that path, which breaks its exact count of loads in flight (it then
+    // over-waits).
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int q = wave * 256 + i * 64 + lane;  // 16-byte chunk of the stage's W2 tiles
-      const int tt = min(t0 + (q >> 10), a.ntiles - 1);
+      const int tt = min(t0 + (q >> 10), t_end - 1);
       ra[d][i] = gload16(W2q + (int64_t)tt * 1024 + (q & 1023));
     }
     const int v = t0 * kTile + lseg * 8;
