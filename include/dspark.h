@@ -18,10 +18,12 @@
  *   - Arguments are checked on the host before anything is enqueued.  On error
  *     the call returns a negative dspark_status, enqueues nothing, leaves the
  *     outputs untouched and records a message for dspark_last_error().
- *   - Values the host cannot see (token ids, confidences) are preconditions:
- *     token ids must lie in [0, V) and confidences in [0, 1]; out-of-range
- *     values give unspecified results but every memory access stays in bounds
- *     (token ids are clamped before they index W1).
+ *   - Values the host cannot see (token ids, confidences, logits) are
+ *     preconditions: token ids must lie in [0, V), confidences in [0, 1], and
+ *     the logits U, T and the weights finite (a logit may be -inf to mask an
+ *     entry); out-of-range values or NaN give unspecified results but every
+ *     memory access stays in bounds (token ids are clamped before they index
+ *     W1).
  *   - dtype: DSPARK_F32 (binary32) or DSPARK_BF16 (bfloat16 bit patterns) for
  *     U, T, W1 and W2.  The Markov-head rank must be 256 (the pages' default).
  *   - Random numbers: Philox4x32-10 (Salmon et al., SC'11) keyed by `seed`,
