@@ -296,3 +296,33 @@ def O_u(U):
     """bf16 bits [R, gamma, V] -> float32 values (test input construction)."""
     from draft_sampling_verification_w1_amd import synth
     return synth.bf16_bits_to_f32(U)
+
+
+def test_masked_logits(dev):
+    """Logits masked with -inf (30% of U and of T): masked entries carry no
+    probability anywhere (draft, c*, residual and bonus draws)."""
+    import torch
+    from oracle import oracle as O
+    from draft_sampling_verification_w1_amd import synth
+    cfg = synth.scaled(synth.CONFIGS["qwen3_4b"], name="masked", R=16, gamma=4, V=3000, n_sps=16 * 5)
+    rng = np.random.default_rng(21)
+    inp = gen_inputs(cfg)
+    U = inp["U"].copy()
+    U[rng.random(U.shape) < 0.3] = 0xFF80  # bf16 -inf
+    inp["U"] = U
+    od = O.draft(U, inp["W1"], inp["W2"], inp["anchors"], cfg.seed)
+    dU, dW1, dA = to_dev(U), to_dev(inp["W1"]), to_dev(inp["anchors"])
+    W2p = dev.pack_w2(to_dev(inp["W2"]), cfg.V)
+    tok, lse, logq = dev.draft_step(dU, dW1, W2p, dA, cfg.seed)
+    torch.cuda.synchronize()
+    n, ties = compare_draft(od, tok.cpu().numpy(), lse.cpu().numpy(), logq.cpu().numpy())
+    assert np.all(U[np.arange(cfg.R)[:, None], np.arange(cfg.gamma)[None, :], tok.cpu().numpy()] != 0xFF80)
+    T = build_target(cfg, inp, od["tokens"])
+    T[rng.random(T.shape) < 0.3] = 0xFF80
+    ov = O.verify(U, inp["W1"], inp["W2"], inp["anchors"], od["tokens"], T, None, cfg.seed)
+    g = dev.verify(dU, dW1, W2p, dA, to_dev(od["tokens"]), to_dev(od["lse"]), to_dev(od["logq"]),
+                   to_dev(T), None, cfg.seed)
+    torch.cuda.synchronize()
+    gn = {k: (v.cpu().numpy() if v is not None else None) for k, v in g.items()}
+    n, ties = compare_verify(ov, gn)
+    log(f"  masked logits: {n} requests compared, {ties} near-ties")
