@@ -5,8 +5,11 @@ One step = one decoding round of the high-concurrency workload (R = 256
 requests, gamma = 16 block positions, V = 151,936, rank-256 Markov head,
 bf16): dspark_draft_step + dspark_verify (all gamma positions verified) +
 dspark_schedule on the round's c* (prefix products and the causal scheduler).
-Inputs are seeded synthetic tensors already resident in HBM when timing
-starts.  Prints one JSON line.
+For a workload with a confidence head (the full scheduled round: R = 512,
+V = 129,280) a step is instead dspark_draft_step + dspark_confidence +
+dspark_schedule on the head's confidences + dspark_verify of the scheduled
+lengths.  Inputs are seeded synthetic tensors already resident in HBM when
+timing starts.  Prints one JSON line.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W]
 """
@@ -45,17 +48,21 @@ def build_target(cfg, synth, U, Ub, W1, W2, anchors, tokens):
     return T
 
 
-def algorithmic_bytes(name, cfg, n_bonus=0):
-    """HBM bytes a launch of kernel `name` must move at minimum (see design notes)."""
+def algorithmic_bytes(name, cfg, n_bonus=0, n_rows=None):
+    """HBM bytes a launch of kernel `name` must move at minimum (see design
+    notes); n_rows = verified rows (default every position)."""
     R, g, V, e = cfg.R, cfg.gamma, cfg.V, (2 if cfg.dtype == "bf16" else 4)
+    rows = R * g if n_rows is None else n_rows
     w2 = 256 * V * e
     w1row = 256 * e
     if name == "draft_bias":      # one position: U_k, gathered W1 rows, W2 once per draft call
         return R * V * e + R * w1row + w2 / g
     if name == "cstar_bias":      # every verified row: U, T, W2, gathered W1 rows
-        return 2 * R * g * V * e + w2 + R * g * w1row
+        return 2 * rows * V * e + w2 + rows * w1row
     if name == "target_lse":      # every verified target row
-        return R * g * V * e
+        return rows * V * e
+    if name == "confidence":      # backbone states of every position
+        return R * g * cfg.confidence_H * 2
     if name == "residual_bias":
         return 2 * R * V * e + w2 + R * w1row
     if name == "bonus":
@@ -63,14 +70,17 @@ def algorithmic_bytes(name, cfg, n_bonus=0):
     return 0.0
 
 
-def path_bytes(cfg, n_bonus):
+def path_bytes(cfg, n_bonus, n_rows=None):
     """Algorithmic HBM bytes of one step: draft (U, W2, W1 rows) + verify (U,
-    verified T rows, bonus rows, W2, W1 rows) + per-row outputs."""
+    verified T rows, bonus rows, W2, W1 rows) + per-row outputs, and the
+    confidence head's backbone states when the step runs it."""
     R, g, V, e = cfg.R, cfg.gamma, cfg.V, (2 if cfg.dtype == "bf16" else 4)
+    rows = R * g if n_rows is None else n_rows
     draft = R * g * V * e + 256 * V * e + R * g * 256 * e
-    verify = 2 * R * g * V * e + n_bonus * V * e + 256 * V * e + R * g * 256 * e
+    verify = 2 * rows * V * e + n_bonus * V * e + 256 * V * e + rows * 256 * e
+    head = R * g * cfg.confidence_H * 2
     outputs = R * g * (4 + 8 + 8 + 4) + R * 8
-    return draft + verify + outputs
+    return draft + verify + head + outputs
 
 
 def measured_traffic(kernel):
@@ -103,23 +113,37 @@ def calibrate_copy(mb):
 
 def cpu_baseline(cfg, synth, inp, T, n_req):
     """The oracle (fp64 CPU) on the first n_req requests of the same workload:
-    the same step as the GPU's (draft, verify of every position, schedule on c*)."""
+    the same step as the GPU's (draft, verify of every position, schedule on c*;
+    with a confidence head: draft, confidence, schedule, verify of the
+    scheduled lengths -- on a sample the scheduler sees the sample's requests only)."""
     from oracle import oracle as O
     req = list(range(n_req))
     U = inp["U"][:n_req]
+    anchors = inp["anchors"][:n_req]
     sps = synth.sps_table(cfg)
+    scheduled = cfg.confidence_H > 0
+    if scheduled:
+        h, w = synth.confidence_inputs(cfg, requests=req)
+        temps = synth.sts_temperatures(cfg)
     t0 = time.perf_counter()
-    od = O.draft(U, inp["W1"], inp["W2"], inp["anchors"][:n_req], cfg.seed)
-    ov = O.verify(U, inp["W1"], inp["W2"], inp["anchors"][:n_req], od["tokens"], T[:n_req], None,
-                  cfg.seed, requests=req)
-    O.schedule(O.prefix_products(np.nan_to_num(ov["cstar"], nan=0.0).astype(np.float32)), sps)
+    od = O.draft(U, inp["W1"], inp["W2"], anchors, cfg.seed)
+    if scheduled:
+        c = O.confidence(h, w, temps, inp["W1"], anchors, od["tokens"])
+        lengths = O.schedule(O.prefix_products(c), sps)["lengths"]
+        O.verify(U, inp["W1"], inp["W2"], anchors, od["tokens"], T[:n_req], lengths, cfg.seed,
+                 requests=req)
+    else:
+        ov = O.verify(U, inp["W1"], inp["W2"], anchors, od["tokens"], T[:n_req], None, cfg.seed,
+                      requests=req)
+        O.schedule(O.prefix_products(np.nan_to_num(ov["cstar"], nan=0.0).astype(np.float32)), sps)
     dt = time.perf_counter() - t0
     cores = int(os.environ.get("OMP_NUM_THREADS") or os.cpu_count())
     what = "the whole batch" if n_req == cfg.R else f"the first {n_req} of {cfg.R} requests"
+    steps = ("draft + confidence + schedule + verify(scheduled lengths)" if scheduled
+             else "draft + verify + schedule")
     return {"value": round(n_req * cfg.gamma / dt, 2), "unit": "positions/s", "cores": cores,
             "kind": "oracle",
-            "sample": f"{what} ({n_req * cfg.gamma} positions): oracle draft + verify + schedule "
-                      f"in fp64, {dt:.1f} s"}
+            "sample": f"{what} ({n_req * cfg.gamma} positions): oracle {steps} in fp64, {dt:.1f} s"}
 
 
 def main():
@@ -185,11 +209,25 @@ def main():
     dT = to_dev(T)
     log(f"[bench] target logits built in {time.time() - t0:.1f}s")
 
+    scheduled = cfg.confidence_H > 0
+    if scheduled:
+        h, w = synth.confidence_inputs(cfg)
+        dH, dWc = to_dev(h), to_dev(w)
+        dTemps = to_dev(synth.sts_temperatures(cfg))
+        c_out = torch.empty((R, g), dtype=torch.float32, device=dev)
+        del h
+
     def step():
         tk, ls, lq = dspark.draft_step(dU, dW1, W2p, dA, cfg.seed, ws=ws, out=d_out)
-        v = dspark.verify(dU, dW1, W2p, dA, tk, ls, lq, dT, None, cfg.seed, ws=ws, out=v_out,
-                          with_mask=False, with_lse_t=False)
-        dspark.schedule(v["cstar"], dSPS, out=s_out, with_path=False)
+        if scheduled:   # the head's confidences set the lengths that verify checks
+            dspark.confidence(dH, dWc, dTemps, dW1, dA, tk, out=c_out)
+            sch = dspark.schedule(c_out, dSPS, out=s_out, with_path=False)
+            dspark.verify(dU, dW1, W2p, dA, tk, ls, lq, dT, sch["lengths"], cfg.seed, ws=ws,
+                          out=v_out, with_mask=False, with_lse_t=False)
+        else:
+            v = dspark.verify(dU, dW1, W2p, dA, tk, ls, lq, dT, None, cfg.seed, ws=ws, out=v_out,
+                              with_mask=False, with_lse_t=False)
+            dspark.schedule(v["cstar"], dSPS, out=s_out, with_path=False)
 
     for _ in range(args.warmup):
         step()
@@ -215,14 +253,16 @@ def main():
     dspark.timing_enable(False)
     kern = dspark.timing_report()
     n_acc = v_out["n_accept"].cpu().numpy()
-    n_bonus = int((n_acc == g).sum())
+    lengths = s_out["lengths"].cpu().numpy() if scheduled else np.full(R, g)
+    n_bonus = int((n_acc == lengths).sum())
     per_step = {k: (c / args.steps, ms_tot / args.steps) for k, (c, ms_tot) in kern.items()}
     dom = max(per_step, key=lambda k: per_step[k][1])
     launches, dom_ms = per_step[dom]
     avg_s = dom_ms / launches * 1e-3
-    nb = algorithmic_bytes(dom, cfg, n_bonus)
+    n_rows = int(lengths.sum())
+    nb = algorithmic_bytes(dom, cfg, n_bonus, n_rows)
     achieved = nb / avg_s / 1e9
-    path_b = path_bytes(cfg, n_bonus)
+    path_b = path_bytes(cfg, n_bonus, n_rows)
     log("[bench] per-step kernel time (ms): " +
         ", ".join(f"{k} {v[1]:.3f} ({v[0]:.0f}x)" for k, v in sorted(per_step.items(), key=lambda x: -x[1][1])))
 
@@ -240,7 +280,9 @@ def main():
         "dtype": cfg.dtype,
         "data": "synthetic",
         "config": {"workload": cfg.name, "R": R, "gamma": g, "V": cfg.V, "rank": cfg.rank,
-                   "step": "draft_step + verify(all gamma positions) + schedule(c*)",
+                   "step": ("draft_step + confidence + schedule(c) + verify(scheduled lengths)"
+                            if scheduled else
+                            "draft_step + verify(all gamma positions) + schedule(c*)"),
                    "path_hbm_bytes": int(path_b),
                    "path_hbm_frac": round(path_b / (ms * 1e-3) / (HBM_PEAK_GBS * 1e9), 4)},
         "roofline": {"kernel": dom, "bound": "hbm", "achieved": round(achieved, 1),
@@ -251,6 +293,8 @@ def main():
         "profiled_ms_per_step": round(prof_ms, 4),
         "mean_accepted": round(float(n_acc.mean()), 3),
     }
+    if scheduled:
+        result["mean_scheduled_length"] = round(float(lengths.mean()), 3)
     if not args.no_cpu_baseline:
         n_cpu = min(args.cpu_requests or R, R)
         log(f"[bench] CPU oracle on {n_cpu} requests ...")

@@ -110,6 +110,7 @@ int bonus_splits(int R, int V) {
 
 struct VerifyLayout {
   BiasGeometry gc, gr;
+  int grid_c, rec_c;  // c* pass: workgroups launched, records per row
   int ns_t, chunk_t, ns_b;
   size_t row_ids, counts, req_off, req_len, req_slot, req_mode, resid_ids, bonus_ids;
   size_t lt_m, lt_s, lse_t, c_s, r_wpos, bytes;
@@ -121,6 +122,11 @@ VerifyLayout verify_layout(const dspark_problem* p) {
   const size_t R = p->R, rows = (size_t)p->R * p->gamma;
   L.gc = bias_geometry(kModeCstar, (int)rows, p->V);
   L.gr = bias_geometry(kModeResidual, p->R, p->V);
+  // the c* pass spreads its workgroups over the row blocks that hold verified
+  // rows (known on the device only): up to one split per workgroup
+  L.grid_c = L.gc.nsplit * L.gc.row_blocks;
+  const int c_stages = ((p->V + kTile - 1) / kTile + L.gc.tiles_per_stage - 1) / L.gc.tiles_per_stage;
+  L.rec_c = L.grid_c < c_stages ? L.grid_c : c_stages;
   L.ns_t = row_split_count((int)rows, p->V, &L.chunk_t);
   L.ns_b = bonus_splits(p->R, p->V);
   Carver c;
@@ -135,7 +141,7 @@ VerifyLayout verify_layout(const dspark_problem* p) {
   L.lt_m = c.take(rows * L.ns_t * sizeof(float));
   L.lt_s = c.take(rows * L.ns_t * sizeof(double));
   L.lse_t = c.take(R * (p->gamma + 1) * sizeof(double));
-  L.c_s = c.take(rows * L.gc.nsplit * sizeof(double));
+  L.c_s = c.take(rows * L.rec_c * sizeof(double));
   L.r_cand = take_cands(c, R * L.gr.nsplit);
   L.r_candf = take_cands(c, R * L.gr.nsplit);
   L.r_wpos = c.take(R * L.gr.nsplit * sizeof(float));
@@ -343,6 +349,7 @@ __attribute__((visibility("default"))) int dspark_draft_step(
   a.vec_ok = rows_vec_ok(p, U, nullptr);
   a.tiles_per_stage = L.g.tiles_per_stage;
   a.nsplit = L.g.nsplit;
+  a.rec_stride = L.g.nsplit;
   a.pm = at<float>(ws, L.pm);
   a.ps = at<double>(ws, L.ps);
   a.cand = cands_at(ws, L.cand);
@@ -413,7 +420,8 @@ __attribute__((visibility("default"))) int dspark_verify(
   w.r_wpos = at<float>(ws, L.r_wpos);
   w.b_cand = cands_at(ws, L.b_cand);
   w.ns_t = L.ns_t;
-  w.ns_c = L.gc.nsplit;
+  w.ns_c = L.rec_c;
+  w.grid_c = L.grid_c;
   w.ns_r = L.gr.nsplit;
   w.ns_b = L.ns_b;
   w.tps_t = L.chunk_t;
@@ -449,6 +457,8 @@ __attribute__((visibility("default"))) int dspark_verify(
   a.nrows = p->R * p->gamma;
   a.tiles_per_stage = L.gc.tiles_per_stage;
   a.nsplit = L.gc.nsplit;
+  a.rec_stride = L.rec_c;
+  a.dyn = 1;
   a.ps = w.c_s;
   e = launch_bias_pass(kModeCstar, bf16, a, s);
   if (e != hipSuccess) return hip_fail(e, "cstar pass");
@@ -458,6 +468,8 @@ __attribute__((visibility("default"))) int dspark_verify(
   a.nrows = p->R;
   a.tiles_per_stage = L.gr.tiles_per_stage;
   a.nsplit = L.gr.nsplit;
+  a.rec_stride = L.gr.nsplit;
+  a.dyn = 0;
   a.ps = nullptr;
   a.cand = w.r_cand;
   a.cand_f = w.r_candf;

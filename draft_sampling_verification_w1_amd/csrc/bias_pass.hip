@@ -32,6 +32,7 @@ namespace {
 
 constexpr int kWaves = 8;
 constexpr int kRowsPerBlock = kWaves * 32;
+static_assert(kRowsPerBlock == 256, "active_split_count assumes 256-row blocks");
 constexpr int kThreads = kWaves * 64;
 constexpr int kTileBytesA = kSteps * 64 * 16;  // one packed W2 tile (16 KB)
 
@@ -256,7 +257,7 @@ __device__ __forceinline__ void epilogue(LaneState<MODE>& st, const float* z, co
 template <int MODE>
 __device__ __forceinline__ void finish(const LaneState<MODE>& st, const RowCtx& rc, int row,
                                        int split, const BiasPassArgs& a, bool writer) {
-  const int64_t o = (int64_t)row * a.nsplit + split;
+  const int64_t o = (int64_t)row * a.rec_stride + split;
   if constexpr (MODE == kModeDraft) {
     if (writer && rc.active) {
       a.pm[o] = st.M;
@@ -284,9 +285,10 @@ __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast
 // tiles to a double-buffered workgroup area, the row segments to the wave's
 // own area (xor-swizzled 16-byte slots); one barrier per stage publishes the
 // W2 tiles.  VEC: rows 16-byte aligned (vector loads), else scalar loads.
-// One (split, row block) of a pass.
+// One (split, row block) of a pass with `nsplit` splits.
 template <int MODE, int D, bool VEC>
-__device__ void bias_body(const BiasPassArgs& a, int split, int row_block, int kpos) {
+__device__ void bias_body(const BiasPassArgs& a, int split, int nsplit, int row_block,
+                          int active_rows, int kpos) {
   constexpr bool kNeedT = MODE != kModeDraft;
   constexpr int ST = 2;
   constexpr int SEG = ST * 64;     // bytes of one row per stage
@@ -303,11 +305,10 @@ __device__ void bias_body(const BiasPassArgs& a, int split, int row_block, int k
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 31;
   const int h = lane >> 5;
-  const int active_rows = a.row_count ? min(*a.row_count, a.nrows) : a.nrows;
   const int row0 = row_block * kRowsPerBlock;
   if (row0 >= active_rows) return;
-  const int t_begin = split_tile(split, a.nsplit, a.ntiles, ST);
-  const int t_end = split_tile(split + 1, a.nsplit, a.ntiles, ST);
+  const int t_begin = split_tile(split, nsplit, a.ntiles, ST);
+  const int t_end = split_tile(split + 1, nsplit, a.ntiles, ST);
   const int c_begin = t_begin / ST;
   const int c_end = (t_end + ST - 1) / ST;
 
@@ -463,9 +464,26 @@ __device__ void bias_body(const BiasPassArgs& a, int split, int row_block, int k
   finish<MODE>(st, rc, row, split, a, h == 0);
 }
 
+// The workgroup's (split, split count, row block).  Static passes: the grid
+// is (splits, row blocks).  With `dyn` the launched workgroups are spread over
+// the row blocks that hold active rows (active_split_count).
+struct PassWork {
+  int split, nsplit, row_block;
+};
+
+__device__ __forceinline__ PassWork pass_work(const BiasPassArgs& a, int active_rows) {
+  if (!a.dyn) return {(int)blockIdx.x, a.nsplit, (int)blockIdx.y};
+  const int grid = (int)(gridDim.x * gridDim.y);
+  const int id = (int)(blockIdx.x + gridDim.x * blockIdx.y);
+  const int ns = active_split_count(grid, active_rows, a.rec_stride);
+  return {id % ns, ns, id / ns};
+}
+
 template <int MODE, int D, bool VEC>
 __global__ __launch_bounds__(kThreads) void k_bias_bf16(const BiasPassArgs a) {
-  bias_body<MODE, D, VEC>(a, blockIdx.x, blockIdx.y, a.k);
+  const int active_rows = a.row_count ? min(*a.row_count, a.nrows) : a.nrows;
+  const PassWork w = pass_work(a, active_rows);
+  bias_body<MODE, D, VEC>(a, w.split, w.nsplit, w.row_block, active_rows, a.k);
 }
 
 // Binary32 rows: same row/lane layout, bias by VALU dot products against the
@@ -478,11 +496,12 @@ __global__ __launch_bounds__(kThreads) void k_bias_f32(const BiasPassArgs a) {
   const int n = lane & 31;
   const int h = lane >> 5;
   const int active_rows = a.row_count ? min(*a.row_count, a.nrows) : a.nrows;
-  const int row0 = blockIdx.y * kRowsPerBlock;
+  const PassWork work = pass_work(a, active_rows);
+  const int row0 = work.row_block * kRowsPerBlock;
   if (row0 >= active_rows) return;
-  const int split = blockIdx.x;
-  const int t_begin = split_tile(split, a.nsplit, a.ntiles, a.tiles_per_stage);
-  const int t_end = split_tile(split + 1, a.nsplit, a.ntiles, a.tiles_per_stage);
+  const int split = work.split;
+  const int t_begin = split_tile(split, work.nsplit, a.ntiles, a.tiles_per_stage);
+  const int t_end = split_tile(split + 1, work.nsplit, a.ntiles, a.tiles_per_stage);
   const f32x4* W2T = reinterpret_cast<const f32x4*>(a.W2p);
   constexpr bool kNeedT = MODE != kModeDraft;
 

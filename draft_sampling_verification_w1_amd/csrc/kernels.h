@@ -68,7 +68,9 @@ struct BiasPassArgs {
   int ntiles;                 // ceil(V / 32)
   int vec_ok;                 // U/T rows 16-byte aligned: vector loads allowed
   int tiles_per_stage;        // tiles per pipeline stage (split granularity)
-  int nsplit;
+  int nsplit;                 // vocabulary splits; with `dyn`, the launched split columns
+  int rec_stride;             // partial records per row (>= every split count the pass uses)
+  int dyn;                    // splits follow the device row count (active_split_count)
   float* pm;                  // draft: running max per partial
   double* ps;                 // draft: sum of exp; cstar: sum of min(p^d, p^t)
   BlockCands cand;            // draft: blocks of p^d; residual: blocks of max(0, p^t - p^d)
@@ -91,6 +93,23 @@ __host__ __device__ inline int split_tile(int s, int nsplit, int ntiles, int tps
   const int st = (int)((int64_t)s * nstages / nsplit);
   const int t = st * tps;
   return t < ntiles ? t : ntiles;
+}
+
+// Splits of a pass whose active row count is known on the device only: the
+// `grid` launched workgroups go to the row blocks (256 rows) that hold active
+// rows, `grid / blocks` vocabulary splits each, at most `max_split`.  The count
+// is rounded down to a multiple of 8 when that idles at most 1/8 of the
+// workgroups: with workgroup id = block * splits + split, every row block of a
+// split then runs on one XCD (ids are dealt to the 8 XCDs in turn) and shares
+// that XCD's L2 copy of the W2 tiles.
+__host__ __device__ inline int active_split_count(int grid, int active_rows, int max_split) {
+  constexpr int kBlockRows = 256;
+  const int blocks = active_rows > kBlockRows ? (active_rows + kBlockRows - 1) / kBlockRows : 1;
+  int ns = grid / blocks;
+  ns = ns < max_split ? ns : max_split;
+  const int ns8 = ns & ~7;
+  if (ns8 > 0 && 8 * (ns - ns8) <= ns) ns = ns8;
+  return ns > 1 ? ns : 1;
 }
 
 hipError_t launch_bias_pass(int mode, bool bf16, const BiasPassArgs& a, hipStream_t stream);
@@ -144,7 +163,8 @@ struct VerifyWs {
   BlockCands r_candf;   // [R*ns_r] its p^t fallback records
   float* r_wpos;        // [R*ns_r]
   BlockCands b_cand;    // [R*ns_b] bonus draw records
-  int ns_t, ns_c, ns_r, ns_b;
+  int ns_t, ns_c, ns_r, ns_b;  // ns_c: c* records per row (their stride)
+  int grid_c;                 // workgroups of the c* pass (active_split_count)
   int tps_t, tps_b;     // elements per split for the row-streaming passes
   int vec_ok;           // T rows 16-byte aligned: vector loads allowed
 };

@@ -298,9 +298,11 @@ __global__ __launch_bounds__(256) void k_finalize(int R, int gamma, VerifyWs w, 
     if (lane == 0) cstar[item] = NAN;
     return;
   }
+  // the c* pass's split count for this many verified rows (records at stride ns_c)
+  const int ns = active_split_count(w.grid_c, min(w.counts[0], R * gamma), w.ns_c);
   const int64_t base = (int64_t)(w.req_off[r] + k - 1) * w.ns_c;
   double s = 0.0;
-  for (int j = lane; j < w.ns_c; j += 64) s += w.c_s[base + j];
+  for (int j = lane; j < ns; j += 64) s += w.c_s[base + j];
 #pragma unroll
   for (int off = 1; off < 64; off <<= 1) s += __shfl_xor(s, off, 64);
   if (lane == 0) cstar[item] = (float)s;

@@ -203,8 +203,9 @@ def verify(U, W1, W2p, anchors, tokens, lse_d, logq, T, lengths, seed: int, ws=N
     return out
 
 
-def confidence(h, w, temps, W1, anchors, tokens, seed: int = 0):
-    """Confidence head with STS (dspark_confidence).  h [R, gamma, H] bf16."""
+def confidence(h, w, temps, W1, anchors, tokens, seed: int = 0, out=None):
+    """Confidence head with STS (dspark_confidence).  h [R, gamma, H] bf16;
+    ``out`` may supply c [R, gamma] fp32 preallocated."""
     R, gamma, H = h.shape
     V = W1.shape[0]
     _need(h, "h", dtype=torch.bfloat16)
@@ -214,7 +215,8 @@ def confidence(h, w, temps, W1, anchors, tokens, seed: int = 0):
     _need(anchors, "anchors", dtype=torch.int32, shape=(R,))
     _need(tokens, "tokens", dtype=torch.int32, shape=(R, gamma))
     p = problem(R, gamma, V, W1.dtype, seed)
-    c = torch.empty((R, gamma), dtype=torch.float32, device=h.device)
+    c = torch.empty((R, gamma), dtype=torch.float32, device=h.device) if out is None else out
+    _need(c, "c", dtype=torch.float32, shape=(R, gamma))
     _check(lib().dspark_confidence(ctypes.byref(p), H, _ptr(h), _ptr(w), _ptr(temps), _ptr(W1),
                                    _ptr(anchors), _ptr(tokens), _ptr(c), _stream()))
     return c
