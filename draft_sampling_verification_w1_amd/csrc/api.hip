@@ -111,7 +111,7 @@ int bonus_splits(int R, int V) {
 struct VerifyLayout {
   BiasGeometry gc, gr;
   int grid_c, rec_c;  // c* pass: workgroups launched, records per row
-  int ns_t, chunk_t, ns_b;
+  int grid_t, ns_t, ns_b;  // target lse: workgroups launched, records per row
   size_t row_ids, counts, req_off, req_len, req_slot, req_mode, resid_ids, bonus_ids;
   size_t lt_m, lt_s, lse_t, c_s, r_wpos, bytes;
   CandLayout r_cand, r_candf, b_cand;
@@ -127,7 +127,11 @@ VerifyLayout verify_layout(const dspark_problem* p) {
   L.grid_c = L.gc.nsplit * L.gc.row_blocks;
   const int c_stages = ((p->V + kTile - 1) / kTile + L.gc.tiles_per_stage - 1) / L.gc.tiles_per_stage;
   L.rec_c = L.grid_c < c_stages ? L.grid_c : c_stages;
-  L.ns_t = row_split_count((int)rows, p->V, &L.chunk_t);
+  // target lse: splits for every position set the grid; fewer verified rows
+  // take more splits each (at most the count for one row: the record stride)
+  int chunk;
+  L.grid_t = (int)rows * lse_split_count((int)rows, 1 << 30, p->V, &chunk);
+  L.ns_t = lse_split_count(1, L.grid_t, p->V, &chunk);
   L.ns_b = bonus_splits(p->R, p->V);
   Carver c;
   L.row_ids = c.take(rows * 4);
@@ -424,8 +428,7 @@ __attribute__((visibility("default"))) int dspark_verify(
   w.grid_c = L.grid_c;
   w.ns_r = L.gr.nsplit;
   w.ns_b = L.ns_b;
-  w.tps_t = L.chunk_t;
-  w.tps_b = 0;
+  w.grid_t = L.grid_t;
   w.vec_ok = rows_vec_ok(p, nullptr, T);
 
   hipError_t e = launch_build_rows(p->R, p->gamma, lengths, w, s);

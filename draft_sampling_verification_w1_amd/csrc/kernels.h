@@ -163,13 +163,27 @@ struct VerifyWs {
   BlockCands r_candf;   // [R*ns_r] its p^t fallback records
   float* r_wpos;        // [R*ns_r]
   BlockCands b_cand;    // [R*ns_b] bonus draw records
-  int ns_t, ns_c, ns_r, ns_b;  // ns_c: c* records per row (their stride)
-  int grid_c;                 // workgroups of the c* pass (active_split_count)
-  int tps_t, tps_b;     // elements per split for the row-streaming passes
+  int ns_t, ns_c, ns_r, ns_b;  // ns_t, ns_c: target-lse / c* records per row (their stride)
+  int grid_t, grid_c;         // workgroups of the target-lse / c* pass (split counts follow the rows)
   int vec_ok;           // T rows 16-byte aligned: vector loads allowed
 };
 
-int row_split_count(int rows, int V, int* chunk);
+// Vocabulary splits of the target-lse pass over `active` rows (known on the
+// device only): about 2048 workgroups in all, at least 2048 entries per split,
+// at most grid / active splits (the launched workgroups), whole 8-entry chunks
+// of *chunk entries.  Never more splits for more rows.
+__host__ __device__ inline int lse_split_count(int active, int grid, int V, int* chunk) {
+  const int rows = active > 1 ? active : 1;
+  int ns = (2048 + rows - 1) / rows;
+  const int max_split = (V + 2047) / 2048;
+  if (ns > max_split) ns = max_split;
+  if (ns > grid / rows) ns = grid / rows;
+  if (ns < 1) ns = 1;
+  int c = (V + ns - 1) / ns;
+  c = (c + 7) & ~7;
+  *chunk = c;
+  return (V + c - 1) / c;
+}
 
 hipError_t launch_build_rows(int R, int gamma, const int32_t* lengths, const VerifyWs& w,
                              hipStream_t stream);

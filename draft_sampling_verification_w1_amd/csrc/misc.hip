@@ -41,7 +41,8 @@ __global__ __launch_bounds__(256) void k_pack_w2_f32(int V, int vpad, const floa
 
 // Confidence head with per-position temperature (summary page §3.2.1):
 // c = sigmoid((w . [h_k; W1[x_{k-1}]]) / T_k), one wave per row, binary64 sums.
-template <typename E>
+// VEC: h rows and w 16-byte aligned (H a multiple of 8), 8 entries per load.
+template <typename E, bool VEC>
 __global__ __launch_bounds__(256) void k_confidence(int R, int gamma, int V, int H,
                                                     const uint16_t* h, const float* w,
                                                     const float* temps, const E* W1,
@@ -56,7 +57,22 @@ __global__ __launch_bounds__(256) void k_confidence(int R, int gamma, int V, int
   x = min(max(x, 0), V - 1);
   const uint16_t* hr = h + (int64_t)row * H;
   double s = 0.0;
-  for (int i = lane; i < H; i += 64) s += (double)w[i] * (double)bf16_at(hr, i);
+  if constexpr (VEC) {
+    for (int i = 8 * lane; i < H; i += 512) {
+      const u32x4 hv = *reinterpret_cast<const u32x4*>(hr + i);
+      const f32x4 wa = *reinterpret_cast<const f32x4*>(w + i);
+      const f32x4 wb = *reinterpret_cast<const f32x4*>(w + i + 4);
+      const float wv[8] = {wa.x, wa.y, wa.z, wa.w, wb.x, wb.y, wb.z, wb.w};
+      const uint32_t hw[4] = {hv.x, hv.y, hv.z, hv.w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const uint32_t bits = (e & 1) ? (hw[e >> 1] & 0xFFFF0000u) : (hw[e >> 1] << 16);
+        s += (double)wv[e] * (double)__uint_as_float(bits);
+      }
+    }
+  } else {
+    for (int i = lane; i < H; i += 64) s += (double)w[i] * (double)bf16_at(hr, i);
+  }
   for (int j = lane; j < kRank; j += 64)
     s += (double)w[H + j] * (double)elem_at(W1, (int64_t)x * kRank + j);
 #pragma unroll
@@ -88,12 +104,19 @@ hipError_t launch_confidence(bool w1_bf16, int R, int gamma, int V, int H, const
   TimingScope timing("confidence", stream);
   const int rows = R * gamma;
   const dim3 grid((rows + 3) / 4);
-  if (w1_bf16)
-    hipLaunchKernelGGL(k_confidence<uint16_t>, grid, dim3(256), 0, stream, R, gamma, V, H, h, w,
-                       temps, (const uint16_t*)W1, anchors, tokens, c);
+  const bool vec = H % 8 == 0 && ((uintptr_t)h & 15u) == 0 && ((uintptr_t)w & 15u) == 0;
+  if (w1_bf16 && vec)
+    hipLaunchKernelGGL((k_confidence<uint16_t, true>), grid, dim3(256), 0, stream, R, gamma, V, H,
+                       h, w, temps, (const uint16_t*)W1, anchors, tokens, c);
+  else if (w1_bf16)
+    hipLaunchKernelGGL((k_confidence<uint16_t, false>), grid, dim3(256), 0, stream, R, gamma, V, H,
+                       h, w, temps, (const uint16_t*)W1, anchors, tokens, c);
+  else if (vec)
+    hipLaunchKernelGGL((k_confidence<float, true>), grid, dim3(256), 0, stream, R, gamma, V, H, h,
+                       w, temps, (const float*)W1, anchors, tokens, c);
   else
-    hipLaunchKernelGGL(k_confidence<float>, grid, dim3(256), 0, stream, R, gamma, V, H, h, w, temps,
-                       (const float*)W1, anchors, tokens, c);
+    hipLaunchKernelGGL((k_confidence<float, false>), grid, dim3(256), 0, stream, R, gamma, V, H, h,
+                       w, temps, (const float*)W1, anchors, tokens, c);
   return hipGetLastError();
 }
 

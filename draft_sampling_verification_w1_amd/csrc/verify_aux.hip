@@ -100,17 +100,24 @@ __global__ __launch_bounds__(1024) void k_build_rows(int R, int gamma, const int
   }
 }
 
+// Workgroup id = verified row * splits + split, the split count following the
+// device row count (lse_split_count; records at stride ns_t).
 template <typename E>
 __global__ __launch_bounds__(256) void k_target_lse(int gamma, int V, const E* T, VerifyWs w) {
-  const int i = blockIdx.x;
-  if (i >= w.counts[0]) return;
+  const int nrows = (int)gridDim.x;  // every position
+  const int active = min(w.counts[0], nrows);
+  int chunk;
+  const int ns = lse_split_count(active, w.grid_t, V, &chunk);
+  const int wg = (int)(blockIdx.x + gridDim.x * blockIdx.y);
+  const int i = wg / ns;
+  if (i >= active) return;
+  const int split = wg - i * ns;
   const int id = w.row_ids[i];
   const int r = id / gamma;
   const int k = id - r * gamma + 1;
   const E* row = T + ((int64_t)r * (gamma + 1) + (k - 1)) * (int64_t)V;
-  const int split = blockIdx.y;
-  const int v0 = split * w.tps_t;
-  const int v1 = min(V, v0 + w.tps_t);
+  const int v0 = split * chunk;
+  const int v1 = min(V, v0 + chunk);
   const bool vec_ok = w.vec_ok != 0;
   float m = -INFINITY;
   double s = 0.0;
@@ -133,7 +140,7 @@ __global__ __launch_bounds__(256) void k_target_lse(int gamma, int V, const E* T
   }
   block_lse(m, s);
   if (threadIdx.x == 0) {
-    const int64_t o = (int64_t)i * w.ns_t + split;
+    const int64_t o = (int64_t)i * w.ns_t + split;  // ns_t: the record stride
     w.lt_m[o] = m;
     w.lt_s[o] = s;
   }
@@ -153,11 +160,13 @@ __global__ __launch_bounds__(256) void k_decide(int R, int gamma, int V, uint64_
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   // 1. lse of each verified target row: wave q merges the split partials of
   //    positions q + 1, q + 5, ... (no workgroup barrier per position)
+  int chunk;
+  const int ns = lse_split_count(min(w.counts[0], R * gamma), w.grid_t, V, &chunk);
   for (int k = wave + 1; k <= L; k += 4) {
     const int64_t base = (int64_t)(off + k - 1) * w.ns_t;
     float m = -INFINITY;
     double s = 0.0;
-    for (int j = lane; j < w.ns_t; j += 64) lse_merge(m, s, w.lt_m[base + j], w.lt_s[base + j]);
+    for (int j = lane; j < ns; j += 64) lse_merge(m, s, w.lt_m[base + j], w.lt_s[base + j]);
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
       const float m2 = __shfl_xor(m, o, 64);
@@ -310,17 +319,6 @@ __global__ __launch_bounds__(256) void k_finalize(int R, int gamma, VerifyWs w, 
 
 }  // namespace
 
-int row_split_count(int rows, int V, int* chunk) {
-  const int max_split = max(1, (V + 2047) / 2048);
-  int ns = max(1, (2048 + rows - 1) / max(rows, 1));
-  ns = min(ns, max_split);
-  int c = (V + ns - 1) / ns;
-  c = (c + 7) & ~7;
-  ns = (V + c - 1) / c;
-  if (chunk) *chunk = c;
-  return ns;
-}
-
 hipError_t launch_build_rows(int R, int gamma, const int32_t* lengths, const VerifyWs& w,
                              hipStream_t stream) {
   TimingScope timing("build_rows", stream);
@@ -331,7 +329,7 @@ hipError_t launch_build_rows(int R, int gamma, const int32_t* lengths, const Ver
 hipError_t launch_target_lse(bool bf16, int R, int gamma, int V, const void* T, const VerifyWs& w,
                              hipStream_t stream) {
   TimingScope timing("target_lse", stream);
-  const dim3 grid(R * gamma, w.ns_t);
+  const dim3 grid(R * gamma, w.grid_t / (R * gamma));  // (positions, splits for every position)
   if (bf16)
     hipLaunchKernelGGL(k_target_lse<uint16_t>, grid, dim3(256), 0, stream, gamma, V,
                        (const uint16_t*)T, w);

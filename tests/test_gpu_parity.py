@@ -141,11 +141,14 @@ def test_pack_layout(dev):
     assert np.all(pf[V:] == 0)
 
 
-def test_confidence_head(dev):
+@pytest.mark.parametrize("H,dtype", [(4096, "bf16"), (1003, "bf16"), (64, "f32")])
+def test_confidence_head(dev, H, dtype):
+    """16-byte loads (H a multiple of 8) and the element path; bf16 and fp32 W1."""
     import torch
     from oracle import oracle as O
     from draft_sampling_verification_w1_amd import synth
-    cfg = synth.scaled(synth.CONFIGS["full_round"], name="conf", R=10, gamma=5, V=3000)
+    cfg = synth.scaled(synth.CONFIGS["full_round"], name="conf", R=10, gamma=5, V=3000,
+                       confidence_H=H, dtype=dtype)
     h, w = synth.confidence_inputs(cfg)
     W1, _ = synth.weights(cfg)
     anchors = synth.anchors(cfg)
