@@ -5,12 +5,10 @@
 //   keeps each request's positions in order), B = sum(1 + l_r),
 //   tau = sum(1 + sum a), Theta = tau * SPS(B); extend while Theta strictly
 //   improves and stop at the first non-improvement (causal stop).
-// One workgroup of 1024 threads: binary32 products per request, a merge sort
-// of the 64-bit keys, an exact integer scan of tau (units of 2^-38) and a
-// parallel search for the first non-improving step.  Because every factor c
-// lies in [0, 1], a request's products never increase with j, so its keys are
-// already an ascending run; the sort only merges runs pairwise (each key finds
-// its place by a binary search in the partner run).
+// One workgroup of 1024 threads: binary32 products per request, a stable
+// radix sort of the candidates by survival (ties keep the (r, j) order), an
+// exact integer scan of tau (units of 2^-38) and a parallel search for the
+// first non-improving step.
 #include "device_common.h"
 #include "kernels.h"
 
@@ -59,24 +57,27 @@ __device__ int64_t block_exclusive_scan(int64_t v, int64_t* wsum, int64_t& total
   return before + x - v;
 }
 
+// E candidates per thread (E * 1024 >= R * gamma).
 template <int E>
 __global__ __launch_bounds__(kThreads) void k_schedule(int R, int gamma, const float* c,
                                                        const float* sps, float* a_out,
                                                        int32_t* lengths, double* stats,
                                                        double* theta_path) {
   __shared__ uint64_t keys[kMaxCand];
+  __shared__ int cnt[64 * kWaves];
   __shared__ int64_t wsum[kWaves];
   __shared__ int first_stop;
   const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
   const int n = R * gamma;
+  constexpr int npad = E * kThreads;
 
   // prefix products, one request per thread (sequential binary32 multiplies;
-  // a request's factors are fetched together, 16 at a time)
+  // a request's factors are fetched together, 16 at a time); the key of
+  // candidate o = r * gamma + j sits at position o
   for (int r = tid; r < R; r += kThreads) {
     const int o0 = r * gamma;
     float acc = 1.0f;
-    uint64_t prev = 0;
-    bool ascending = true;
     for (int j0 = 0; j0 < gamma; j0 += 16) {
       float cc[16];
 #pragma unroll
@@ -87,80 +88,55 @@ __global__ __launch_bounds__(kThreads) void k_schedule(int R, int gamma, const f
           const int o = o0 + j0 + u;
           acc = __fmul_rn(acc, cc[u]);
           a_out[o] = acc;
-          const uint64_t key = ((uint64_t)survival_key_hi(acc) << 32) | (uint32_t)o;
-          ascending = ascending && (o == o0 || key > prev);
-          prev = key;
-          keys[o] = key;
+          keys[o] = ((uint64_t)survival_key_hi(acc) << 32) | (uint32_t)o;
         }
-      }
-    }
-    // a factor above 1 (a c* rounded up past 1, say) can break the run: sort
-    // the request's own keys (insertion sort, the run is nearly in order)
-    if (!ascending) {
-      for (int i = o0 + 1; i < o0 + gamma; ++i) {
-        const uint64_t x = keys[i];
-        int j = i - 1;
-        while (j >= o0 && keys[j] > x) {
-          keys[j + 1] = keys[j];
-          --j;
-        }
-        keys[j + 1] = x;
       }
     }
     lengths[r] = 0;
   }
+  for (int p = n + tid; p < npad; p += kThreads) keys[p] = ~(uint64_t)0;  // after every real key
   if (tid == 0) first_stop = n;
   __syncthreads();
 
-  // merge runs pairwise: run m covers [m*L, min((m+1)*L, n)); an element of
-  // run m moves to (start of the pair) + (its place in run m) + (keys of the
-  // partner run below it).  Keys are distinct, so the order is total.
-  const int base = E * tid;
-  uint64_t e[E];
-  int run0[E];  // run of each of the thread's positions at the first level
-#pragma unroll
-  for (int q = 0; q < E; ++q) run0[q] = (base + q) / gamma;
-  int level = 0;
-  for (int L = gamma; L < n; L <<= 1, ++level) {
-    // binary search of each key in the partner run (fixed number of steps)
-    int dest[E], lo[E], len[E];
+  // stable LSD radix sort on the 30 bits of survival_key_hi, 6 bits (64 digits)
+  // per pass.  Wave w holds positions w*64E + q*64 + lane (q < E), so the
+  // order (wave, q, lane) is the position order.  A key's new place = the
+  // offset of (its digit, its wave) + the keys of that digit before it in the
+  // wave: lane d keeps the running count of digit d over q, and ballots of
+  // the digit bits rank the lanes within one q.
+  const uint64_t below = (1ull << lane) - 1ull;
+  for (int shift = 32; shift < 62; shift += 6) {
+    uint64_t e[E];
+    int dig[E], rank[E];
+    int run = 0;
 #pragma unroll
     for (int q = 0; q < E; ++q) {
-      const int p = base + q;
-      dest[q] = 0;
-      lo[q] = 0;
-      len[q] = 0;
-      if (p < n) {
-        e[q] = keys[p];
-        const int m = run0[q] >> level;
-        const int pair = (m >> 1) * 2 * L;
-        const int plo = (m & 1) ? pair : min(pair + L, n);
-        const int phi = (m & 1) ? pair + L : min(pair + 2 * L, n);
-        dest[q] = pair + (p - m * L) - plo;  // + index of the first partner key >= e[q]
-        lo[q] = plo;
-        len[q] = phi - plo;
-      }
-    }
-    for (int steps = 32 - __builtin_clz(L); steps > 0; --steps) {
+      e[q] = keys[wave * 64 * E + q * 64 + lane];
+      const int d = (int)(e[q] >> shift) & 63;
+      dig[q] = d;
+      uint64_t mine = ~0ull, of_lane = ~0ull;
 #pragma unroll
-      for (int q = 0; q < E; ++q) {
-        if (len[q] > 0) {
-          const int half = len[q] >> 1;
-          if (keys[lo[q] + half] < e[q]) {
-            lo[q] += half + 1;
-            len[q] -= half + 1;
-          } else {
-            len[q] = half;
-          }
-        }
+      for (int i = 0; i < 6; ++i) {
+        const uint64_t b = __ballot((d >> i) & 1);
+        mine &= ((d >> i) & 1) ? b : ~b;
+        of_lane &= ((lane >> i) & 1) ? b : ~b;
       }
+      rank[q] = __shfl(run, d, 64) + __popcll(mine & below);
+      run += __popcll(of_lane);
     }
+    cnt[lane * kWaves + wave] = run;
+    __syncthreads();
+    int64_t total;
+    // each thread scans and then overwrites its own entry: (digit, wave) order
+    const int64_t off = block_exclusive_scan(cnt[tid], wsum, total);
+    cnt[tid] = (int)off;
     __syncthreads();
 #pragma unroll
-    for (int q = 0; q < E; ++q)
-      if (base + q < n) keys[dest[q] + lo[q]] = e[q];
+    for (int q = 0; q < E; ++q) keys[cnt[dig[q] * kWaves + wave] + rank[q]] = e[q];
     __syncthreads();
   }
+  const int base = E * tid;
+  uint64_t e[E];
 #pragma unroll
   for (int q = 0; q < E; ++q) e[q] = base + q < n ? keys[base + q] : ~(uint64_t)0;
 

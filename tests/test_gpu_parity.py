@@ -182,6 +182,34 @@ def test_schedule_against_oracle(dev, R, gamma):
         compare_schedule(os_, gs["a"].cpu().numpy(), {k: v.cpu().numpy() for k, v in gs.items() if k != "a"})
 
 
+@pytest.mark.parametrize("R,gamma", [(37, 5), (256, 16), (512, 16), (1024, 16)])
+def test_schedule_ties(dev, R, gamma):
+    """Factors from {1/4, 1/2, 3/4, 1}: many survival products are equal, across
+    requests and within one, so the (r, j) order of equal keys decides which
+    candidates fill the first places.  Lengths, statistics and the Theta path
+    must equal the oracle's exactly."""
+    import torch
+    from oracle import oracle as O
+    from draft_sampling_verification_w1_amd import synth
+    cfg = synth.scaled(synth.CONFIGS["full_round"], name="sched_ties", R=R, gamma=gamma,
+                       n_sps=R * (gamma + 1))
+    rng = np.random.default_rng(R * 100 + gamma)
+    c = rng.choice(np.array([0.25, 0.5, 0.75, 1.0], np.float32), (R, gamma), p=[0.1, 0.2, 0.3, 0.4])
+    a = O.prefix_products(c)
+    assert len(np.unique(a)) < a.size // 2, "too few ties: the case is not exercised"
+    for sps in [synth.sps_table(cfg),
+                (1000.0 * np.minimum(1.0, (R + R * gamma // 3) / np.arange(1, R * (gamma + 1) + 1))).astype(np.float32)]:
+        os_ = O.schedule(a, sps)
+        gs = dev.schedule(to_dev(c), to_dev(sps))
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(gs["a"].cpu().numpy(), a)
+        np.testing.assert_array_equal(gs["lengths"].cpu().numpy(), os_["lengths"])
+        np.testing.assert_array_equal(gs["stats"].cpu().numpy(), os_["stats"])
+        np.testing.assert_array_equal(gs["theta_path"].cpu().numpy(), os_["theta_path"])
+        n_sel = int(os_["stats"][3])
+        assert 0 < n_sel < R * gamma, f"stop at {n_sel}: the cut is not exercised"
+
+
 def test_schedule_factor_above_one(dev):
     """A factor just above 1 (a c* rounded up past 1, say) makes a request's
     products rise by an ulp, so its positions are no longer in key order.  The
