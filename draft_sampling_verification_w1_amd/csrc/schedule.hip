@@ -71,6 +71,22 @@ __global__ __launch_bounds__(kThreads) void k_schedule(int R, int gamma, const f
   const int lane = tid & 63, wave = tid >> 6;
   const int n = R * gamma;
   constexpr int npad = E * kThreads;
+  const int base = E * tid;  // the thread's sorted positions base .. base + E - 1
+
+  // the stop test's table entries SPS(R + i) for i = base - 1 .. base + E - 1:
+  // their positions are known now, so the loads overlap the sort (at E = 16
+  // the registers are short, and they are loaded where they are used)
+  constexpr bool kEarly = E <= 8;
+  float sp[kEarly ? E + 1 : 1];
+  if constexpr (kEarly) {
+#pragma unroll
+    for (int q = 0; q <= E; ++q) sp[q] = (base + q <= n) ? sps[R + base + q - 1] : 0.0f;
+  }
+  auto sps_at = [&](int q) -> float {
+    if constexpr (kEarly) return sp[q];
+    else return sps[R + base + q - 1];
+  };
+  const float sps_r = sps[R - 1];
 
   // prefix products, one request per thread (sequential binary32 multiplies;
   // a request's factors are fetched together, 16 at a time); the key of
@@ -92,7 +108,6 @@ __global__ __launch_bounds__(kThreads) void k_schedule(int R, int gamma, const f
         }
       }
     }
-    lengths[r] = 0;
   }
   for (int p = n + tid; p < npad; p += kThreads) keys[p] = ~(uint64_t)0;  // after every real key
   if (tid == 0) first_stop = n;
@@ -102,29 +117,32 @@ __global__ __launch_bounds__(kThreads) void k_schedule(int R, int gamma, const f
   // per pass.  Wave w holds positions w*64E + q*64 + lane (q < E), so the
   // order (wave, q, lane) is the position order.  A key's new place = the
   // offset of (its digit, its wave) + the keys of that digit before it in the
-  // wave: lane d keeps the running count of digit d over q, and ballots of
-  // the digit bits rank the lanes within one q.
+  // wave.  Ballots of the digit bits give each lane the lanes of its q with
+  // the same digit; the lowest of them adds the group to the wave's counter of
+  // that digit (cnt[digit][wave], touched by this wave alone, in program
+  // order) and hands the previous count to the group.
   const uint64_t below = (1ull << lane) - 1ull;
   for (int shift = 32; shift < 62; shift += 6) {
     uint64_t e[E];
     int dig[E], rank[E];
-    int run = 0;
+    cnt[lane * kWaves + wave] = 0;  // digit = lane
 #pragma unroll
     for (int q = 0; q < E; ++q) {
       e[q] = keys[wave * 64 * E + q * 64 + lane];
       const int d = (int)(e[q] >> shift) & 63;
       dig[q] = d;
-      uint64_t mine = ~0ull, of_lane = ~0ull;
+      uint64_t same = ~0ull;
 #pragma unroll
       for (int i = 0; i < 6; ++i) {
         const uint64_t b = __ballot((d >> i) & 1);
-        mine &= ((d >> i) & 1) ? b : ~b;
-        of_lane &= ((lane >> i) & 1) ? b : ~b;
+        same &= ((d >> i) & 1) ? b : ~b;
       }
-      rank[q] = __shfl(run, d, 64) + __popcll(mine & below);
-      run += __popcll(of_lane);
+      const int before = __popcll(same & below);
+      const int leader = __ffsll((unsigned long long)same) - 1;
+      int prior = 0;
+      if (before == 0) prior = atomicAdd(&cnt[d * kWaves + wave], __popcll(same));
+      rank[q] = __shfl(prior, leader, 64) + before;
     }
-    cnt[lane * kWaves + wave] = run;
     __syncthreads();
     int64_t total;
     // each thread scans and then overwrites its own entry: (digit, wave) order
@@ -135,7 +153,6 @@ __global__ __launch_bounds__(kThreads) void k_schedule(int R, int gamma, const f
     for (int q = 0; q < E; ++q) keys[cnt[dig[q] * kWaves + wave] + rank[q]] = e[q];
     __syncthreads();
   }
-  const int base = E * tid;
   uint64_t e[E];
 #pragma unroll
   for (int q = 0; q < E; ++q) e[q] = base + q < n ? keys[base + q] : ~(uint64_t)0;
@@ -146,17 +163,21 @@ __global__ __launch_bounds__(kThreads) void k_schedule(int R, int gamma, const f
   for (int q = 0; q < E; ++q) local += base + q < n ? tau_unit(e[q]) : 0;
   int64_t total;
   const int64_t offset = block_exclusive_scan(local, wsum, total);
+  // every thread has its keys in registers now (the scan's barrier): the key
+  // array holds the per-request lengths from here on
+  int* len = reinterpret_cast<int*>(keys);
+  for (int r = tid; r < R; r += kThreads) len[r] = 0;
   const int64_t tau0 = (int64_t)R << 38;
-  const double theta0 = (double)R * (double)sps[R - 1];
+  const double theta0 = (double)R * (double)sps_r;
   int64_t tau = tau0 + offset;  // before element base
   int my_stop = n;
 #pragma unroll
   for (int q = 0; q < E; ++q) {
     const int i = base + q;
     if (i < n) {
-      const double before = ldexp((double)tau, -38) * (double)sps[R + i - 1];
+      const double before = ldexp((double)tau, -38) * (double)sps_at(q);
       tau += tau_unit(e[q]);
-      const double after = ldexp((double)tau, -38) * (double)sps[R + i];
+      const double after = ldexp((double)tau, -38) * (double)sps_at(q + 1);
       if (!(after > before) && my_stop == n) my_stop = i;
     }
   }
@@ -172,8 +193,8 @@ __global__ __launch_bounds__(kThreads) void k_schedule(int R, int gamma, const f
     if (i < n) {
       const uint32_t o = (uint32_t)e[q];
       tau += tau_unit(e[q]);
-      const double th = ldexp((double)tau, -38) * (double)sps[R + i];
-      if (i < sel) atomicMax(&lengths[o / gamma], (int)(o % gamma) + 1);
+      const double th = ldexp((double)tau, -38) * (double)sps_at(q + 1);
+      if (i < sel) atomicMax(&len[o / gamma], (int)(o % gamma) + 1);
       if (theta_path) theta_path[i + 1] = (i <= sel) ? th : NAN;
       if (i == sel - 1) {
         stats[0] = (double)(R + sel);
@@ -183,6 +204,8 @@ __global__ __launch_bounds__(kThreads) void k_schedule(int R, int gamma, const f
       }
     }
   }
+  __syncthreads();
+  for (int r = tid; r < R; r += kThreads) lengths[r] = len[r];
   if (tid == 0) {
     if (theta_path) theta_path[0] = theta0;
     if (sel == 0) {
