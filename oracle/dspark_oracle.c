@@ -432,3 +432,142 @@ ORACLE_API int64_t oracle_schedule(int64_t R, int64_t gamma, const float* a,
   free(cand);
   return sel;
 }
+
+/* ------------------------------------------------------------------------ */
+/* Production variant of the prefix scheduler.  [P1 §5.2]                    */
+/* The deployed scheduler fits Algorithm 1 to an irregular, discontinuous    */
+/* SPS(B) curve and to zero-overhead scheduling: the capacity K of a round   */
+/* is chosen from confidences of two rounds earlier, and the round's own      */
+/* candidates are ranked by their current survival probability, of which the */
+/* first K are verified.  When the capacity is predicted from past rounds     */
+/* the early-stopping break is left out, so that a throughput cliff does not  */
+/* trap the search in a local optimum.                                        */
+/* READINGS: the capacity is the number of candidates, taken in the order of  */
+/* Algorithm 1, at which Theta is largest along the whole path (l = 0 up to   */
+/* every candidate); the smallest such count wins ties.  tau and Theta are    */
+/* formed exactly as in Algorithm 1.                                          */
+/* ------------------------------------------------------------------------ */
+static cand_t* sorted_candidates(int64_t R, int64_t gamma, const float* a) {
+  const int64_t n = R * gamma;
+  cand_t* cand = (cand_t*)malloc((size_t)(n > 0 ? n : 1) * sizeof(cand_t));
+  for (int64_t r = 0; r < R; ++r)
+    for (int64_t j = 1; j <= gamma; ++j) {
+      cand[r * gamma + (j - 1)].a = a[r * gamma + (j - 1)];
+      cand[r * gamma + (j - 1)].r = (int32_t)r;
+      cand[r * gamma + (j - 1)].j = (int32_t)j;
+    }
+  qsort(cand, (size_t)n, sizeof(cand_t), cand_cmp);
+  return cand;
+}
+
+/* Capacity: returns K (or -1 if the SPS table is too short); stats = (B, tau,
+ * Theta, K) at K; theta_path[i] = Theta after the first i candidates, i = 0..n
+ * (every entry: there is no stop). */
+ORACLE_API int64_t oracle_schedule_capacity(int64_t R, int64_t gamma, const float* a,
+                                            const float* sps, int64_t n_sps, double* stats,
+                                            double* theta_path) {
+  const int64_t n = R * gamma;
+  if (n_sps < R * (gamma + 1)) return -1;
+  cand_t* cand = sorted_candidates(R, gamma, a);
+  int64_t tau_units = R * ((int64_t)1 << 38);
+  double best = ldexp((double)tau_units, -38) * (double)sps[R - 1];
+  int64_t best_i = 0, best_tau = tau_units;
+  if (theta_path) theta_path[0] = best;
+  for (int64_t i = 0; i < n; ++i) {
+    tau_units += oracle_tau_units(cand[i].a);
+    const double theta = ldexp((double)tau_units, -38) * (double)sps[R + i];  /* SPS(R+i+1) */
+    if (theta_path) theta_path[i + 1] = theta;
+    if (theta > best) {  /* strict: the smallest count wins ties */
+      best = theta;
+      best_i = i + 1;
+      best_tau = tau_units;
+    }
+  }
+  stats[0] = (double)(R + best_i);
+  stats[1] = ldexp((double)best_tau, -38);
+  stats[2] = best;
+  stats[3] = (double)best_i;
+  free(cand);
+  return best_i;
+}
+
+/* Top-K: verify the first min(K, n) candidates in survival order (K >= 0);
+ * lengths [R]; stats = (B, tau, Theta, taken) with Theta = tau * SPS(B). */
+ORACLE_API int64_t oracle_schedule_topk(int64_t R, int64_t gamma, const float* a,
+                                        const float* sps, int64_t n_sps, int64_t K,
+                                        int32_t* lengths, double* stats) {
+  const int64_t n = R * gamma;
+  if (n_sps < R * (gamma + 1) || K < 0) return -1;
+  cand_t* cand = sorted_candidates(R, gamma, a);
+  const int64_t take = K < n ? K : n;
+  for (int64_t r = 0; r < R; ++r) lengths[r] = 0;
+  int64_t tau_units = R * ((int64_t)1 << 38);
+  for (int64_t i = 0; i < take; ++i) {
+    tau_units += oracle_tau_units(cand[i].a);
+    lengths[cand[i].r] = cand[i].j;  /* order respects prefixes */
+  }
+  stats[0] = (double)(R + take);
+  stats[1] = ldexp((double)tau_units, -38);
+  stats[2] = stats[1] * (double)sps[R + take - 1];
+  stats[3] = (double)take;
+  free(cand);
+  return take;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Static-threshold verification and per-position conditional acceptance.   */
+/* [P1 §4.3.3, §4.3.1]                                                       */
+/* The threshold experiment verifies, per request, the prefix whose          */
+/* estimated survival stays at or above a fixed threshold; READING: l_r is   */
+/* the largest j with a_{r,i} >= theta for every i <= j (the prefix form,    */
+/* equal to max{j : a_{r,j} >= theta} when a is non-increasing).             */
+/* ------------------------------------------------------------------------ */
+ORACLE_API void oracle_threshold_lengths(int64_t R, int64_t gamma, const float* a,
+                                         double theta, int32_t* lengths) {
+  for (int64_t r = 0; r < R; ++r) {
+    int32_t l = 0;
+    while (l < gamma && (double)a[r * gamma + l] >= theta) ++l;
+    lengths[r] = l;
+  }
+}
+
+/* Conditional acceptance at position k counts only rollouts whose earlier
+ * draft tokens were all accepted [P1 §4.3.1].  mask [R, gamma]: 1 accepted,
+ * 0 rejected, 255 not verified.  reached[k-1] = requests whose positions
+ * 1..k-1 are accepted and whose position k was verified; accepted[k-1] = those
+ * of them that accepted position k. */
+ORACLE_API void oracle_conditional_acceptance(int64_t R, int64_t gamma, const uint8_t* mask,
+                                              int64_t* reached, int64_t* accepted) {
+  for (int64_t k = 0; k < gamma; ++k) reached[k] = accepted[k] = 0;
+  for (int64_t r = 0; r < R; ++r) {
+    for (int64_t k = 0; k < gamma; ++k) {
+      int prefix_ok = 1;
+      for (int64_t i = 0; i < k; ++i)
+        if (mask[r * gamma + i] != 1) prefix_ok = 0;
+      if (!prefix_ok || mask[r * gamma + k] == 255) continue;
+      reached[k] += 1;
+      if (mask[r * gamma + k] == 1) accepted[k] += 1;
+    }
+  }
+}
+
+/* Threshold sweep over one fully verified round: for each threshold, the
+ * tokens a threshold-limited verify would check, sum_r l_r(theta), and the
+ * draft tokens it would accept, sum_r min(n_r, l_r(theta)), where n_r is the
+ * accepted length of the full verify (acceptance at a position does not depend
+ * on how far the verify reaches). */
+ORACLE_API void oracle_threshold_sweep(int64_t R, int64_t gamma, const float* a,
+                                       const int32_t* n_accept, int64_t n_thr,
+                                       const double* thresholds, int64_t* verified,
+                                       int64_t* accepted) {
+  int32_t* l = (int32_t*)malloc((size_t)(R > 0 ? R : 1) * sizeof(int32_t));
+  for (int64_t g = 0; g < n_thr; ++g) {
+    oracle_threshold_lengths(R, gamma, a, thresholds[g], l);
+    verified[g] = accepted[g] = 0;
+    for (int64_t r = 0; r < R; ++r) {
+      verified[g] += l[r];
+      accepted[g] += n_accept[r] < l[r] ? n_accept[r] : l[r];
+    }
+  }
+  free(l);
+}

@@ -39,6 +39,7 @@ _f32p = ctypes.POINTER(ctypes.c_float)
 _i32p = ctypes.POINTER(ctypes.c_int32)
 _u32p = ctypes.POINTER(ctypes.c_uint32)
 _u8p = ctypes.POINTER(ctypes.c_uint8)
+_i64p = ctypes.POINTER(ctypes.c_int64)
 
 
 def build(force: bool = True) -> str:
@@ -95,6 +96,18 @@ def lib() -> ctypes.CDLL:
         L.oracle_schedule.argtypes = [ctypes.c_int64, ctypes.c_int64, _f32p, _f32p,
                                       ctypes.c_int64, _i32p, _f64p, _f64p, _f64p]
         L.oracle_schedule.restype = ctypes.c_int64
+        L.oracle_schedule_capacity.argtypes = [ctypes.c_int64, ctypes.c_int64, _f32p, _f32p,
+                                               ctypes.c_int64, _f64p, _f64p]
+        L.oracle_schedule_capacity.restype = ctypes.c_int64
+        L.oracle_schedule_topk.argtypes = [ctypes.c_int64, ctypes.c_int64, _f32p, _f32p,
+                                           ctypes.c_int64, ctypes.c_int64, _i32p, _f64p]
+        L.oracle_schedule_topk.restype = ctypes.c_int64
+        L.oracle_threshold_lengths.argtypes = [ctypes.c_int64, ctypes.c_int64, _f32p,
+                                               ctypes.c_double, _i32p]
+        L.oracle_conditional_acceptance.argtypes = [ctypes.c_int64, ctypes.c_int64, _u8p,
+                                                    _i64p, _i64p]
+        L.oracle_threshold_sweep.argtypes = [ctypes.c_int64, ctypes.c_int64, _f32p, _i32p,
+                                             ctypes.c_int64, _f64p, _i64p, _i64p]
         _lib = L
     return _lib
 
@@ -353,3 +366,70 @@ def schedule(a: np.ndarray, sps: np.ndarray):
         raise ValueError("SPS table shorter than R*(gamma+1)")
     return {"lengths": lengths, "stats": stats, "theta_path": path, "stop_gap": gap.value,
             "n_sel": int(sel)}
+
+
+# ---------------------------------------------------------------------------
+# production scheduler: capacity from past rounds, top-K now  [P1 §5.2]
+# ---------------------------------------------------------------------------
+def schedule_capacity(a: np.ndarray, sps: np.ndarray):
+    """Capacity K: the candidate count (survival order) with the largest Theta
+    along the whole path, no early stop; returns dict K, stats, theta_path."""
+    a = np.ascontiguousarray(a, dtype=np.float32)
+    sps = np.ascontiguousarray(sps, dtype=np.float32)
+    R, gamma = a.shape
+    stats = np.zeros(4, np.float64)
+    path = np.full(R * gamma + 1, np.nan)
+    K = lib().oracle_schedule_capacity(R, gamma, _p(a, _f32p), _p(sps, _f32p), sps.size,
+                                       _p(stats, _f64p), _p(path, _f64p))
+    if K < 0:
+        raise ValueError("SPS table shorter than R*(gamma+1)")
+    return {"K": int(K), "stats": stats, "theta_path": path}
+
+
+def schedule_topk(a: np.ndarray, sps: np.ndarray, K: int):
+    """Verify the first min(K, R*gamma) candidates in survival order."""
+    a = np.ascontiguousarray(a, dtype=np.float32)
+    sps = np.ascontiguousarray(sps, dtype=np.float32)
+    R, gamma = a.shape
+    lengths = np.zeros(R, np.int32)
+    stats = np.zeros(4, np.float64)
+    t = lib().oracle_schedule_topk(R, gamma, _p(a, _f32p), _p(sps, _f32p), sps.size, int(K),
+                                   _p(lengths, _i32p), _p(stats, _f64p))
+    if t < 0:
+        raise ValueError("SPS table shorter than R*(gamma+1), or K < 0")
+    return {"lengths": lengths, "stats": stats}
+
+
+# ---------------------------------------------------------------------------
+# static threshold, conditional acceptance, threshold sweep  [P1 §4.3.1, §4.3.3]
+# ---------------------------------------------------------------------------
+def threshold_lengths(a: np.ndarray, theta: float) -> np.ndarray:
+    a = np.ascontiguousarray(a, dtype=np.float32)
+    R, gamma = a.shape
+    lengths = np.zeros(R, np.int32)
+    lib().oracle_threshold_lengths(R, gamma, _p(a, _f32p), float(theta), _p(lengths, _i32p))
+    return lengths
+
+
+def conditional_acceptance(mask: np.ndarray):
+    """(reached[k], accepted[k]) per position from an accept mask [R, gamma]."""
+    mask = np.ascontiguousarray(mask, dtype=np.uint8)
+    R, gamma = mask.shape
+    reached = np.zeros(gamma, np.int64)
+    accepted = np.zeros(gamma, np.int64)
+    lib().oracle_conditional_acceptance(R, gamma, _p(mask, _u8p), _p(reached, _i64p),
+                                        _p(accepted, _i64p))
+    return reached, accepted
+
+
+def threshold_sweep(a: np.ndarray, n_accept: np.ndarray, thresholds):
+    """(verified[g], accepted[g]) for each threshold of a fully verified round."""
+    a = np.ascontiguousarray(a, dtype=np.float32)
+    na = np.ascontiguousarray(n_accept, dtype=np.int32)
+    th = np.ascontiguousarray(thresholds, dtype=np.float64)
+    R, gamma = a.shape
+    ver = np.zeros(th.size, np.int64)
+    acc = np.zeros(th.size, np.int64)
+    lib().oracle_threshold_sweep(R, gamma, _p(a, _f32p), _p(na, _i32p), th.size, _p(th, _f64p),
+                                 _p(ver, _i64p), _p(acc, _i64p))
+    return ver, acc
