@@ -146,6 +146,56 @@ def cpu_baseline(cfg, synth, inp, T, n_req):
             "sample": f"{what} ({n_req * cfg.gamma} positions): oracle {steps} in fp64, {dt:.1f} s"}
 
 
+def scheduler_variants(cfg, dspark, synth, steps, warmup):
+    """Per-call time of the production scheduler (capacity from the round two
+    earlier, top-K on the current round), the static threshold and the
+    acceptance statistics at the workload's R and gamma.  Inputs: seeded
+    confidences; the accept mask follows them (position k accepted with
+    probability c_k, until the first rejection)."""
+    import torch
+    R, g = cfg.R, cfg.gamma
+    dev = torch.device("cuda:0")
+    cs = [synth.survival_inputs(cfg, index=i) for i in range(3)]
+    rng = np.random.default_rng(cfg.seed)
+    acc = rng.random((R, g)) < cs[2]
+    mask = np.full((R, g), 255, np.uint8)
+    for r in range(R):
+        for k in range(g):
+            mask[r, k] = 1 if acc[r, k] else 0
+            if not acc[r, k]:
+                break
+    n_acc = (np.cumprod(acc, axis=1)).sum(axis=1).astype(np.int32)
+    dc = [torch.from_numpy(c).to(dev) for c in cs]
+    dmask = torch.from_numpy(mask).to(dev)
+    dn = torch.from_numpy(n_acc).to(dev)
+    thr = torch.linspace(0.0, 1.0, 64, dtype=torch.float64, device=dev)
+    sps = torch.from_numpy(synth.sps_table(cfg)).to(dev)
+
+    def one():
+        cap = dspark.schedule_capacity(dc[0], sps, with_path=False)   # round t-2
+        top = dspark.schedule_topk(dc[2], cap["K"], sps)               # round t
+        th = dspark.schedule_threshold(dc[2], 0.5)
+        dspark.acceptance_stats(dmask, top["a"], dn, thr)
+        return cap, top, th
+
+    for _ in range(warmup):
+        one()
+    torch.cuda.synchronize()
+    dspark.timing_enable(True)
+    for _ in range(steps):
+        cap, top, th = one()
+    torch.cuda.synchronize()
+    dspark.timing_enable(False)
+    kern = dspark.timing_report()
+    return {"metric": "scheduler variants: microseconds per call", "unit": "us",
+            "higher_is_better": False, "n_gpus": 1, "steps": steps, "data": "synthetic",
+            "config": {"workload": cfg.name, "R": R, "gamma": g, "n_thresholds": 64},
+            "kernels_us": {k: round(ms * 1e3 / n, 2) for k, (n, ms) in kern.items()},
+            "capacity_K": int(cap["K"].cpu()[0]),
+            "topk_B": float(top["stats"][0].cpu()),
+            "threshold_mean_length": float(th["lengths"].float().mean().cpu())}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -157,6 +207,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="first run a plain device copy of MIB MiB (counter calibration)")
+    ap.add_argument("--scheduler-variants", action="store_true",
+                    help="time the production scheduler, static threshold and acceptance "
+                         "statistics instead of the round (one JSON line of its own)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -173,6 +226,9 @@ def main():
     dspark.lib()
     if args.calibrate_copy:
         calibrate_copy(args.calibrate_copy)
+    if args.scheduler_variants:
+        print(json.dumps(scheduler_variants(cfg, dspark, synth, args.steps, args.warmup)), flush=True)
+        return
     tdt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
 
     def to_dev(a):

@@ -549,4 +549,74 @@ __attribute__((visibility("default"))) int dspark_schedule(int32_t R, int32_t ga
   return ok();
 }
 
+__attribute__((visibility("default"))) int dspark_schedule_capacity(
+    int32_t R, int32_t gamma, const float* c, const float* sps, int32_t n_sps, float* a,
+    int32_t* K, int32_t* lengths, double* stats, double* theta_path, void* stream) {
+  if (R < 1 || gamma < 1) return fail(DSPARK_ERR_SHAPE, "R=%d, gamma=%d must be >= 1", R, gamma);
+  if ((int64_t)R * gamma > 16384)
+    return fail(DSPARK_ERR_SHAPE, "R*gamma=%lld exceeds 16384", (long long)R * gamma);
+  if ((int64_t)n_sps < (int64_t)R * (gamma + 1))
+    return fail(DSPARK_ERR_RANGE, "SPS table has %d entries, R*(gamma+1)=%lld needed", n_sps,
+                (long long)R * (gamma + 1));
+  if (!c || !sps || !a || !K || !lengths || !stats)
+    return fail(DSPARK_ERR_ARG, "schedule_capacity: tensor pointers must be non-NULL");
+  hipError_t e = launch_schedule_capacity(R, gamma, c, sps, a, K, lengths, stats, theta_path,
+                                          (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "schedule_capacity");
+  return ok();
+}
+
+__attribute__((visibility("default"))) int dspark_schedule_topk(int32_t R, int32_t gamma,
+                                                                const float* c, const int32_t* K,
+                                                                const float* sps, int32_t n_sps,
+                                                                float* a, int32_t* lengths,
+                                                                double* stats, void* stream) {
+  if (R < 1 || gamma < 1) return fail(DSPARK_ERR_SHAPE, "R=%d, gamma=%d must be >= 1", R, gamma);
+  if ((int64_t)R * gamma > 16384)
+    return fail(DSPARK_ERR_SHAPE, "R*gamma=%lld exceeds 16384", (long long)R * gamma);
+  if ((int64_t)n_sps < (int64_t)R * (gamma + 1))
+    return fail(DSPARK_ERR_RANGE, "SPS table has %d entries, R*(gamma+1)=%lld needed", n_sps,
+                (long long)R * (gamma + 1));
+  if (!c || !K || !sps || !a || !lengths || !stats)
+    return fail(DSPARK_ERR_ARG, "schedule_topk: tensor pointers must be non-NULL");
+  hipError_t e = launch_schedule_topk(R, gamma, c, K, sps, a, lengths, stats, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "schedule_topk");
+  return ok();
+}
+
+__attribute__((visibility("default"))) int dspark_schedule_threshold(int32_t R, int32_t gamma,
+                                                                     const float* c, double theta,
+                                                                     float* a, int32_t* lengths,
+                                                                     void* stream) {
+  if (R < 1 || R > 65536 || gamma < 1 || gamma > 64)
+    return fail(DSPARK_ERR_SHAPE, "R=%d, gamma=%d outside [1, 65536] x [1, 64]", R, gamma);
+  if (theta != theta) return fail(DSPARK_ERR_RANGE, "threshold is NaN");
+  if (!c || !a || !lengths)
+    return fail(DSPARK_ERR_ARG, "schedule_threshold: tensor pointers must be non-NULL");
+  hipError_t e = launch_threshold(R, gamma, c, theta, a, lengths, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "schedule_threshold");
+  return ok();
+}
+
+__attribute__((visibility("default"))) int dspark_acceptance_stats(
+    int32_t R, int32_t gamma, const uint8_t* accept_mask, const float* a,
+    const int32_t* n_accept, const double* thresholds, int32_t n_thr, int64_t* reached,
+    int64_t* accepted, int64_t* sweep_verified, int64_t* sweep_accepted, void* stream) {
+  if (R < 1 || R > 65536 || gamma < 1 || gamma > 64)
+    return fail(DSPARK_ERR_SHAPE, "R=%d, gamma=%d outside [1, 65536] x [1, 64]", R, gamma);
+  if (n_thr < 0 || n_thr > kMaxThresholds)
+    return fail(DSPARK_ERR_SHAPE, "n_thr=%d outside [0, %d]", n_thr, kMaxThresholds);
+  if (!accept_mask && n_thr == 0)
+    return fail(DSPARK_ERR_ARG, "acceptance_stats: nothing to compute");
+  if (accept_mask && (!reached || !accepted))
+    return fail(DSPARK_ERR_ARG, "acceptance_stats: reached and accepted must be non-NULL");
+  if (n_thr > 0 && (!a || !n_accept || !thresholds || !sweep_verified || !sweep_accepted))
+    return fail(DSPARK_ERR_ARG, "acceptance_stats: sweep pointers must be non-NULL");
+  hipError_t e = launch_acceptance_stats(R, gamma, accept_mask, a, n_accept, thresholds, n_thr,
+                                         reached, accepted, sweep_verified, sweep_accepted,
+                                         (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "acceptance_stats");
+  return ok();
+}
+
 }  // extern "C"

@@ -206,5 +206,20 @@ hipError_t launch_confidence(bool w1_bf16, int R, int gamma, int V, int H, const
 hipError_t launch_schedule(int R, int gamma, const float* c, const float* sps, float* a,
                            int32_t* lengths, double* stats, double* theta_path,
                            hipStream_t stream);
+hipError_t launch_schedule_capacity(int R, int gamma, const float* c, const float* sps,
+                                    float* a, int32_t* K, int32_t* lengths, double* stats,
+                                    double* theta_path, hipStream_t stream);
+hipError_t launch_schedule_topk(int R, int gamma, const float* c, const int32_t* K,
+                                const float* sps, float* a, int32_t* lengths, double* stats,
+                                hipStream_t stream);
+
+// ---- static threshold and acceptance statistics ---------------------------
+constexpr int kMaxThresholds = 1024;
+hipError_t launch_threshold(int R, int gamma, const float* c, double theta, float* a,
+                            int32_t* lengths, hipStream_t stream);
+hipError_t launch_acceptance_stats(int R, int gamma, const uint8_t* mask, const float* a,
+                                   const int32_t* n_accept, const double* thresholds, int n_thr,
+                                   int64_t* reached, int64_t* accepted, int64_t* sweep_verified,
+                                   int64_t* sweep_accepted, hipStream_t stream);
 
 }  // namespace dspark

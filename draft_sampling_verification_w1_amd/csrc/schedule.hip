@@ -9,6 +9,13 @@
 // radix sort of the candidates by survival (ties keep the (r, j) order), an
 // exact integer scan of tau (units of 2^-38) and a parallel search for the
 // first non-improving step.
+//
+// The same kernel serves the production variant (summary page §5.2): the
+// capacity K of a later round is the candidate count with the largest Theta
+// along the whole survival-ordered path (no early-stopping break, so a cliff
+// in an irregular SPS curve does not end the search; the smallest count wins
+// ties), and a round with a capacity handed to it verifies its first K
+// candidates in current survival order (top-K).
 #include "device_common.h"
 #include "kernels.h"
 
@@ -19,6 +26,7 @@ namespace {
 constexpr int kMaxCand = 16384;
 constexpr int kThreads = 1024;
 constexpr int kWaves = kThreads / 64;
+constexpr int kAlg1 = 0, kCapacity = 1, kTopK = 2;
 
 __device__ __forceinline__ uint32_t survival_key_hi(float a) {
   const uint32_t b = __float_as_uint(a);
@@ -57,16 +65,19 @@ __device__ int64_t block_exclusive_scan(int64_t v, int64_t* wsum, int64_t& total
   return before + x - v;
 }
 
-// E candidates per thread (E * 1024 >= R * gamma).
-template <int E>
+// E candidates per thread (E * 1024 >= R * gamma).  MODE: kAlg1 (causal
+// stop), kCapacity (argmax of Theta over the whole path; K written to
+// k_io[0]), kTopK (the first min(k_io[0], R*gamma) candidates).
+template <int E, int MODE>
 __global__ __launch_bounds__(kThreads) void k_schedule(int R, int gamma, const float* c,
                                                        const float* sps, float* a_out,
                                                        int32_t* lengths, double* stats,
-                                                       double* theta_path) {
+                                                       double* theta_path, int32_t* k_io) {
   __shared__ uint64_t keys[kMaxCand];
   __shared__ int cnt[64 * kWaves];
   __shared__ int64_t wsum[kWaves];
   __shared__ int first_stop;
+  __shared__ unsigned long long best_bits;
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int n = R * gamma;
@@ -110,7 +121,14 @@ __global__ __launch_bounds__(kThreads) void k_schedule(int R, int gamma, const f
     }
   }
   for (int p = n + tid; p < npad; p += kThreads) keys[p] = ~(uint64_t)0;  // after every real key
-  if (tid == 0) first_stop = n;
+  if (tid == 0) {
+    // kTopK: the count handed over (clamped to [0, n]); otherwise n = "no stop yet"
+    int k0 = n;
+    if constexpr (MODE == kTopK) k0 = min(max(k_io[0], 0), n);
+    first_stop = k0;
+    // Theta >= 0 (a, SPS >= 0), so the bit patterns of the doubles order as the values
+    best_bits = (unsigned long long)__double_as_longlong((double)R * (double)sps_r);
+  }
   __syncthreads();
 
   // stable LSD radix sort on the 30 bits of survival_key_hi, 6 bits (64 digits)
@@ -170,20 +188,50 @@ __global__ __launch_bounds__(kThreads) void k_schedule(int R, int gamma, const f
   const int64_t tau0 = (int64_t)R << 38;
   const double theta0 = (double)R * (double)sps_r;
   int64_t tau = tau0 + offset;  // before element base
-  int my_stop = n;
+  if constexpr (MODE == kAlg1) {
+    int my_stop = n;
 #pragma unroll
-  for (int q = 0; q < E; ++q) {
-    const int i = base + q;
-    if (i < n) {
-      const double before = ldexp((double)tau, -38) * (double)sps_at(q);
-      tau += tau_unit(e[q]);
-      const double after = ldexp((double)tau, -38) * (double)sps_at(q + 1);
-      if (!(after > before) && my_stop == n) my_stop = i;
+    for (int q = 0; q < E; ++q) {
+      const int i = base + q;
+      if (i < n) {
+        const double before = ldexp((double)tau, -38) * (double)sps_at(q);
+        tau += tau_unit(e[q]);
+        const double after = ldexp((double)tau, -38) * (double)sps_at(q + 1);
+        if (!(after > before) && my_stop == n) my_stop = i;
+      }
     }
+    if (my_stop < n) atomicMin(&first_stop, my_stop);
+  } else if constexpr (MODE == kCapacity) {
+    // the largest Theta after any count i + 1 = 1..n (count 0 seeded above),
+    // then the smallest count that reaches it
+    double th[E];
+    double mx = 0.0;
+#pragma unroll
+    for (int q = 0; q < E; ++q) {
+      const int i = base + q;
+      th[q] = -1.0;
+      if (i < n) {
+        tau += tau_unit(e[q]);
+        th[q] = ldexp((double)tau, -38) * (double)sps_at(q + 1);
+        mx = fmax(mx, th[q]);
+      }
+    }
+    atomicMax(&best_bits, (unsigned long long)__double_as_longlong(mx));
+    __syncthreads();
+    const double best = __longlong_as_double((long long)best_bits);
+    if (tid == 0 && (double)R * (double)sps_r == best) atomicMin(&first_stop, 0);
+#pragma unroll
+    for (int q = 0; q < E; ++q)
+      if (th[q] == best) {
+        atomicMin(&first_stop, base + q + 1);
+        break;
+      }
   }
-  if (my_stop < n) atomicMin(&first_stop, my_stop);
   __syncthreads();
   const int sel = first_stop;
+  if constexpr (MODE == kCapacity) {
+    if (tid == 0) k_io[0] = sel;
+  }
 
   // lengths: every selected candidate raises its request's length
   tau = tau0 + offset;
@@ -195,7 +243,9 @@ __global__ __launch_bounds__(kThreads) void k_schedule(int R, int gamma, const f
       tau += tau_unit(e[q]);
       const double th = ldexp((double)tau, -38) * (double)sps_at(q + 1);
       if (i < sel) atomicMax(&len[o / gamma], (int)(o % gamma) + 1);
-      if (theta_path) theta_path[i + 1] = (i <= sel) ? th : NAN;
+      // Algorithm 1 records the path up to and including the stopping step;
+      // the capacity search records all of it
+      if (theta_path) theta_path[i + 1] = (MODE == kCapacity || i <= sel) ? th : NAN;
       if (i == sel - 1) {
         stats[0] = (double)(R + sel);
         stats[1] = ldexp((double)tau, -38);
@@ -219,21 +269,50 @@ __global__ __launch_bounds__(kThreads) void k_schedule(int R, int gamma, const f
 
 }  // namespace
 
+template <int MODE>
+static void launch_mode(int R, int gamma, const float* c, const float* sps, float* a,
+                        int32_t* lengths, double* stats, double* theta_path, int32_t* k_io,
+                        hipStream_t stream) {
+  const int64_t n = (int64_t)R * gamma;
+  if (n <= 4 * kThreads)
+    hipLaunchKernelGGL((k_schedule<4, MODE>), dim3(1), dim3(kThreads), 0, stream, R, gamma, c,
+                       sps, a, lengths, stats, theta_path, k_io);
+  else if (n <= 8 * kThreads)
+    hipLaunchKernelGGL((k_schedule<8, MODE>), dim3(1), dim3(kThreads), 0, stream, R, gamma, c,
+                       sps, a, lengths, stats, theta_path, k_io);
+  else
+    hipLaunchKernelGGL((k_schedule<16, MODE>), dim3(1), dim3(kThreads), 0, stream, R, gamma, c,
+                       sps, a, lengths, stats, theta_path, k_io);
+}
+
 hipError_t launch_schedule(int R, int gamma, const float* c, const float* sps, float* a,
                            int32_t* lengths, double* stats, double* theta_path,
                            hipStream_t stream) {
   const int64_t n = (int64_t)R * gamma;
   if (n < 1 || n > kMaxCand) return hipErrorInvalidValue;
   TimingScope timing("schedule", stream);
-  if (n <= 4 * kThreads)
-    hipLaunchKernelGGL(k_schedule<4>, dim3(1), dim3(kThreads), 0, stream, R, gamma, c, sps, a,
-                       lengths, stats, theta_path);
-  else if (n <= 8 * kThreads)
-    hipLaunchKernelGGL(k_schedule<8>, dim3(1), dim3(kThreads), 0, stream, R, gamma, c, sps, a,
-                       lengths, stats, theta_path);
-  else
-    hipLaunchKernelGGL(k_schedule<16>, dim3(1), dim3(kThreads), 0, stream, R, gamma, c, sps, a,
-                       lengths, stats, theta_path);
+  launch_mode<kAlg1>(R, gamma, c, sps, a, lengths, stats, theta_path, nullptr, stream);
+  return hipGetLastError();
+}
+
+hipError_t launch_schedule_capacity(int R, int gamma, const float* c, const float* sps,
+                                    float* a, int32_t* K, int32_t* lengths, double* stats,
+                                    double* theta_path, hipStream_t stream) {
+  const int64_t n = (int64_t)R * gamma;
+  if (n < 1 || n > kMaxCand) return hipErrorInvalidValue;
+  TimingScope timing("schedule_capacity", stream);
+  launch_mode<kCapacity>(R, gamma, c, sps, a, lengths, stats, theta_path, K, stream);
+  return hipGetLastError();
+}
+
+hipError_t launch_schedule_topk(int R, int gamma, const float* c, const int32_t* K,
+                                const float* sps, float* a, int32_t* lengths, double* stats,
+                                hipStream_t stream) {
+  const int64_t n = (int64_t)R * gamma;
+  if (n < 1 || n > kMaxCand) return hipErrorInvalidValue;
+  TimingScope timing("schedule_topk", stream);
+  launch_mode<kTopK>(R, gamma, c, sps, a, lengths, stats, nullptr, const_cast<int32_t*>(K),
+                     stream);
   return hipGetLastError();
 }
 

@@ -20,7 +20,9 @@ _DTYPES = {torch.float32: F32, torch.bfloat16: BF16}
 
 SYMBOLS = ("dspark_w2_packed_bytes", "dspark_pack_w2", "dspark_workspace_bytes",
            "dspark_draft_step", "dspark_verify", "dspark_confidence", "dspark_schedule",
-           "dspark_last_error", "dspark_timing_enable", "dspark_timing_report")
+           "dspark_schedule_capacity", "dspark_schedule_topk", "dspark_schedule_threshold",
+           "dspark_acceptance_stats", "dspark_last_error", "dspark_timing_enable",
+           "dspark_timing_report")
 
 
 class Problem(ctypes.Structure):
@@ -58,11 +60,21 @@ def lib() -> ctypes.CDLL:
         L.dspark_confidence.argtypes = [P, ctypes.c_int32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]
         L.dspark_schedule.argtypes = [ctypes.c_int32, ctypes.c_int32, _vp, _vp, ctypes.c_int32, _vp,
                                       _vp, _vp, _vp, _vp]
+        L.dspark_schedule_capacity.argtypes = [ctypes.c_int32, ctypes.c_int32, _vp, _vp,
+                                               ctypes.c_int32, _vp, _vp, _vp, _vp, _vp, _vp]
+        L.dspark_schedule_topk.argtypes = [ctypes.c_int32, ctypes.c_int32, _vp, _vp, _vp,
+                                           ctypes.c_int32, _vp, _vp, _vp, _vp]
+        L.dspark_schedule_threshold.argtypes = [ctypes.c_int32, ctypes.c_int32, _vp,
+                                                ctypes.c_double, _vp, _vp, _vp]
+        L.dspark_acceptance_stats.argtypes = [ctypes.c_int32, ctypes.c_int32, _vp, _vp, _vp, _vp,
+                                              ctypes.c_int32, _vp, _vp, _vp, _vp, _vp]
         L.dspark_last_error.restype = ctypes.c_char_p
         L.dspark_timing_enable.argtypes = [ctypes.c_int]
         L.dspark_timing_report.argtypes = [ctypes.c_char_p, ctypes.c_size_t]
         for name in ("dspark_pack_w2", "dspark_draft_step", "dspark_verify", "dspark_confidence",
-                     "dspark_schedule", "dspark_timing_enable", "dspark_timing_report"):
+                     "dspark_schedule", "dspark_schedule_capacity", "dspark_schedule_topk",
+                     "dspark_schedule_threshold", "dspark_acceptance_stats",
+                     "dspark_timing_enable", "dspark_timing_report"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -238,4 +250,80 @@ def schedule(c, sps, with_path: bool = True, out=None):
     _check(lib().dspark_schedule(R, gamma, _ptr(c), _ptr(sps), sps.numel(), _ptr(out["a"]),
                                  _ptr(out["lengths"]), _ptr(out["stats"]), _ptr(out["theta_path"]),
                                  _stream()))
+    return out
+
+
+def schedule_capacity(c, sps, with_path: bool = True):
+    """Production scheduler, capacity (dspark_schedule_capacity): K = the
+    candidate count with the largest Theta along the whole path (no early
+    stop), left on the device in out["K"]."""
+    R, gamma = c.shape
+    _need(c, "c", dtype=torch.float32)
+    _need(sps, "sps", dtype=torch.float32)
+    dev = c.device
+    out = {"a": torch.empty((R, gamma), dtype=torch.float32, device=dev),
+           "K": torch.empty(1, dtype=torch.int32, device=dev),
+           "lengths": torch.empty(R, dtype=torch.int32, device=dev),
+           "stats": torch.empty(4, dtype=torch.float64, device=dev),
+           "theta_path": torch.empty(R * gamma + 1, dtype=torch.float64, device=dev)
+           if with_path else None}
+    _check(lib().dspark_schedule_capacity(R, gamma, _ptr(c), _ptr(sps), sps.numel(),
+                                          _ptr(out["a"]), _ptr(out["K"]), _ptr(out["lengths"]),
+                                          _ptr(out["stats"]), _ptr(out["theta_path"]), _stream()))
+    return out
+
+
+def schedule_topk(c, K, sps):
+    """Production scheduler, top-K (dspark_schedule_topk); K is a device int32
+    tensor of one element."""
+    R, gamma = c.shape
+    _need(c, "c", dtype=torch.float32)
+    _need(K, "K", dtype=torch.int32)
+    _need(sps, "sps", dtype=torch.float32)
+    dev = c.device
+    out = {"a": torch.empty((R, gamma), dtype=torch.float32, device=dev),
+           "lengths": torch.empty(R, dtype=torch.int32, device=dev),
+           "stats": torch.empty(4, dtype=torch.float64, device=dev)}
+    _check(lib().dspark_schedule_topk(R, gamma, _ptr(c), _ptr(K), _ptr(sps), sps.numel(),
+                                      _ptr(out["a"]), _ptr(out["lengths"]), _ptr(out["stats"]),
+                                      _stream()))
+    return out
+
+
+def schedule_threshold(c, theta: float):
+    """Static-threshold verify lengths (dspark_schedule_threshold)."""
+    R, gamma = c.shape
+    _need(c, "c", dtype=torch.float32)
+    out = {"a": torch.empty((R, gamma), dtype=torch.float32, device=c.device),
+           "lengths": torch.empty(R, dtype=torch.int32, device=c.device)}
+    _check(lib().dspark_schedule_threshold(R, gamma, _ptr(c), float(theta), _ptr(out["a"]),
+                                           _ptr(out["lengths"]), _stream()))
+    return out
+
+
+def acceptance_stats(accept_mask=None, a=None, n_accept=None, thresholds=None):
+    """Per-position conditional acceptance counts and a threshold sweep
+    (dspark_acceptance_stats).  accept_mask [R, gamma] uint8 or None; a [R,
+    gamma] fp32, n_accept [R] int32 and thresholds [n] fp64 for the sweep."""
+    ref = accept_mask if accept_mask is not None else a
+    R, gamma = ref.shape
+    dev = ref.device
+    out = {}
+    if accept_mask is not None:
+        _need(accept_mask, "accept_mask", dtype=torch.uint8)
+        out["reached"] = torch.empty(gamma, dtype=torch.int64, device=dev)
+        out["accepted"] = torch.empty(gamma, dtype=torch.int64, device=dev)
+    n_thr = 0
+    if thresholds is not None:
+        _need(a, "a", dtype=torch.float32)
+        _need(n_accept, "n_accept", dtype=torch.int32)
+        _need(thresholds, "thresholds", dtype=torch.float64)
+        n_thr = thresholds.numel()
+        out["sweep_verified"] = torch.empty(n_thr, dtype=torch.int64, device=dev)
+        out["sweep_accepted"] = torch.empty(n_thr, dtype=torch.int64, device=dev)
+    _check(lib().dspark_acceptance_stats(R, gamma, _ptr(accept_mask), _ptr(a), _ptr(n_accept),
+                                         _ptr(thresholds), n_thr, _ptr(out.get("reached")),
+                                         _ptr(out.get("accepted")),
+                                         _ptr(out.get("sweep_verified")),
+                                         _ptr(out.get("sweep_accepted")), _stream()))
     return out

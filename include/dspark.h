@@ -146,6 +146,56 @@ int dspark_confidence(const dspark_problem* p, int32_t H, const uint16_t* h, con
 int dspark_schedule(int32_t R, int32_t gamma, const float* c, const float* sps, int32_t n_sps,
                     float* a, int32_t* lengths, double* stats, double* theta_path, void* stream);
 
+/* Production variant of the scheduler: capacity.  [P1 §5.2]
+ * The deployed scheduler sets a round's capacity K from confidences two
+ * rounds old and leaves out the early-stopping break, so that the search is
+ * not caught in a local optimum at a throughput cliff of an irregular SPS(B).
+ * Here: a = prefix products of c (as in dspark_schedule), candidates in the
+ * same survival order, Theta_i = tau_i * sps[R+i-1] after the first i
+ * candidates (i = 0..R*gamma, tau as in dspark_schedule); K = the smallest i
+ * with the largest Theta_i, written to K[0] on the device (a later round reads
+ * it there with no host synchronisation).  lengths [R]: the top-K verify
+ * lengths on these same confidences; stats [4] = (B, tau, Theta, K) at K;
+ * theta_path [R*gamma+1] float64 or NULL: every Theta_i.  sps entries must be
+ * finite and >= 0.  Limit: R*gamma <= 16384. */
+int dspark_schedule_capacity(int32_t R, int32_t gamma, const float* c, const float* sps,
+                             int32_t n_sps, float* a, int32_t* K, int32_t* lengths,
+                             double* stats, double* theta_path, void* stream);
+
+/* Production variant of the scheduler: top-K.  [P1 §5.2]
+ * Verify the first min(K[0], R*gamma) candidates (K[0] < 0 counts as 0) in the
+ * survival order of this round's c; K is a device int32 (normally written by
+ * dspark_schedule_capacity two rounds earlier).  a [R, gamma] float32;
+ * lengths [R] int32 (prefixes, since a request's survival never rises);
+ * stats [4] = (B, tau, Theta, taken), Theta = tau * sps[B-1].
+ * Limit: R*gamma <= 16384. */
+int dspark_schedule_topk(int32_t R, int32_t gamma, const float* c, const int32_t* K,
+                         const float* sps, int32_t n_sps, float* a, int32_t* lengths,
+                         double* stats, void* stream);
+
+/* Static-threshold verify lengths.  [P1 §4.3.3]
+ * a = binary32 prefix products of c [R, gamma]; lengths[r] = the largest j
+ * with a[r,i-1] >= theta (compared in binary64) for every i <= j.
+ * theta must not be NaN.  Limits: 1 <= R <= 65536, 1 <= gamma <= 64. */
+int dspark_schedule_threshold(int32_t R, int32_t gamma, const float* c, double theta, float* a,
+                              int32_t* lengths, void* stream);
+
+/* Acceptance statistics of one verified round.  [P1 §4.3.1, §4.3.3]
+ * accept_mask [R, gamma] (dspark_verify's: 1 accepted, 0 rejected, 255 not
+ * verified) or NULL.  Position k counts only rollouts whose positions 1..k-1
+ * were all accepted: reached[k-1] = requests with positions 1..k-1 accepted
+ * and position k verified, accepted[k-1] = those that accepted position k
+ * (int64 [gamma] each).  Threshold sweep (n_thr in [0, 1024]; a [R, gamma]
+ * survival products, n_accept [R] the accepted lengths of a verify of all
+ * gamma positions, thresholds [n_thr] float64): sweep_verified[g] = sum_r
+ * l_r(thresholds[g]) with l_r as in dspark_schedule_threshold, and
+ * sweep_accepted[g] = sum_r min(n_accept[r], l_r) -- the tokens a verify
+ * limited by that threshold checks and accepts.  One workgroup; no workspace. */
+int dspark_acceptance_stats(int32_t R, int32_t gamma, const uint8_t* accept_mask, const float* a,
+                            const int32_t* n_accept, const double* thresholds, int32_t n_thr,
+                            int64_t* reached, int64_t* accepted, int64_t* sweep_verified,
+                            int64_t* sweep_accepted, void* stream);
+
 /* Message for the last failing call on this thread ("" if none). */
 const char* dspark_last_error(void);
 

@@ -105,3 +105,24 @@ def test_binding_refuses_cpu_tensors(L):
     U = torch.zeros((1, 1, 8))
     with pytest.raises(ValueError):
         L._need(U, "U")
+
+
+def test_production_and_threshold_validation(L):
+    lib = L.lib()
+    fake = ctypes.c_void_p(0x1000)
+    # capacity / top-K: same shape and table checks as Algorithm 1, K pointer required
+    assert lib.dspark_schedule_capacity(0, 4, fake, fake, 100, fake, fake, fake, fake, None, None) == -2
+    assert lib.dspark_schedule_capacity(4, 8, fake, fake, 35, fake, fake, fake, fake, None, None) == -5
+    assert lib.dspark_schedule_capacity(4, 8, fake, fake, 36, fake, None, fake, fake, None, None) == -1
+    assert lib.dspark_schedule_topk(1025, 16, fake, fake, fake, 10 ** 6, fake, fake, fake, None) == -2
+    assert lib.dspark_schedule_topk(4, 8, fake, None, fake, 36, fake, fake, fake, None) == -1
+    assert lib.dspark_schedule_topk(4, 8, fake, fake, fake, 35, fake, fake, fake, None) == -5
+    # threshold: NaN threshold and shapes
+    assert lib.dspark_schedule_threshold(4, 65, fake, 0.5, fake, fake, None) == -2
+    assert lib.dspark_schedule_threshold(4, 8, fake, float("nan"), fake, fake, None) == -5
+    assert lib.dspark_schedule_threshold(4, 8, None, 0.5, fake, fake, None) == -1
+    # acceptance statistics
+    assert lib.dspark_acceptance_stats(4, 8, None, None, None, None, 0, None, None, None, None, None) == -1
+    assert lib.dspark_acceptance_stats(4, 8, fake, None, None, None, 1025, fake, fake, fake, fake, None) == -2
+    assert lib.dspark_acceptance_stats(4, 8, fake, None, None, fake, 3, fake, fake, fake, fake, None) == -1
+    assert b"sweep" in lib.dspark_last_error()
