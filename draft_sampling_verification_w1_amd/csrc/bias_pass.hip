@@ -24,6 +24,7 @@
 // the lane pair (n, n+32).
 // Binary32 rows compute the same bias with a VALU dot product.
 #include "device_common.h"
+#include "draft_epilogue.h"
 #include "kernels.h"
 
 namespace dspark {
@@ -130,46 +131,11 @@ __device__ __forceinline__ u32x4 gload16(const void* p) {
   return *(global_u32x4*)(p);
 }
 
-__device__ __forceinline__ void decode16(u32x4 a, u32x4 b, float* out) {
-  const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    out[2 * i] = bf16_lo(w[i]);
-    out[2 * i + 1] = bf16_hi(w[i]);
-  }
-}
-
-__device__ __forceinline__ float sum16(const float* e) {
-  float a0 = (e[0] + e[1]) + (e[2] + e[3]);
-  float a1 = (e[4] + e[5]) + (e[6] + e[7]);
-  float a2 = (e[8] + e[9]) + (e[10] + e[11]);
-  float a3 = (e[12] + e[13]) + (e[14] + e[15]);
-  return (a0 + a1) + (a2 + a3);
-}
-
-__device__ __forceinline__ float max16(const float* z) {
-  float a0 = fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3]));
-  float a1 = fmaxf(fmaxf(z[4], z[5]), fmaxf(z[6], z[7]));
-  float a2 = fmaxf(fmaxf(z[8], z[9]), fmaxf(z[10], z[11]));
-  float a3 = fmaxf(fmaxf(z[12], z[13]), fmaxf(z[14], z[15]));
-  return fmaxf(fmaxf(a0, a1), fmaxf(a2, a3));
-}
-
 template <int MODE>
 struct LaneState;
 
 template <>
-struct LaneState<kModeDraft> {
-  float M;        // running max of z over the split
-  double S;       // sum of exp(z - M)
-  CandState cand;
-  u32x4 words;    // Philox block holding the current block's variate
-  __device__ void init() {
-    M = -INFINITY;
-    S = 0.0;
-    cand.init();
-  }
-};
+struct LaneState<kModeDraft> : DraftLane {};
 
 template <>
 struct LaneState<kModeCstar> {
@@ -198,23 +164,7 @@ template <int MODE>
 __device__ __forceinline__ void epilogue(LaneState<MODE>& st, const float* z, const float* tv,
                                          const RowCtx& rc, int t, bool first, uint64_t seed) {
   if constexpr (MODE == kModeDraft) {
-    if (first || (t & 3) == 0) st.words = noise_block(seed, kStreamDraft, rc.r, rc.k, (uint32_t)t >> 2);
-    const float mt = max_halves(max16(z));
-    if (mt == -INFINITY) return;  // block without mass
-    const float mt2 = mt * kLog2e;
-    float e[16];
-#pragma unroll
-    for (int j = 0; j < 16; ++j) e[j] = __builtin_amdgcn_exp2f(fmaf(z[j], kLog2e, -mt2));
-    const float s = sum_halves(sum16(e));
-    if (mt > st.M) {
-      st.S = st.S * (double)__builtin_amdgcn_exp2f((st.M - mt) * kLog2e) + (double)s;
-      st.M = mt;
-    } else {
-      st.S += (double)(s * __builtin_amdgcn_exp2f((mt - st.M) * kLog2e));
-    }
-    const float sc = fmaf(__builtin_amdgcn_logf(s), kLn2, mt) + gumbel_f32(word_of(st.words, t & 3));
-    const float d = fmaf(kScoreRel, fabsf(mt), kScoreAbs);
-    st.cand.add(sc - d, sc + d, t);
+    draft_block_epilogue(st, z, rc.r, rc.k, t, first, seed);
   } else if constexpr (MODE == kModeCstar) {
     float e[16];
 #pragma unroll

@@ -1,0 +1,76 @@
+// draft_epilogue.h -- the draft's per-tile epilogue, shared by the split bias
+// pass and the persistent draft kernel: for one row and one 32-token block
+// (lane pair n, n + 32, 16 logits each) the running log-sum-exp of
+// z = U_k + B_k and the block's score log-mass + Gumbel variate, bracketed by
+// its binary32 error bound, for the first level of the two-level Gumbel-max
+// draw from p_k = softmax(z) (summary page §3.1).
+#pragma once
+
+#include "device_common.h"
+
+namespace dspark {
+
+__device__ __forceinline__ float sum16(const float* e) {
+  float a0 = (e[0] + e[1]) + (e[2] + e[3]);
+  float a1 = (e[4] + e[5]) + (e[6] + e[7]);
+  float a2 = (e[8] + e[9]) + (e[10] + e[11]);
+  float a3 = (e[12] + e[13]) + (e[14] + e[15]);
+  return (a0 + a1) + (a2 + a3);
+}
+
+__device__ __forceinline__ float max16(const float* z) {
+  float a0 = fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3]));
+  float a1 = fmaxf(fmaxf(z[4], z[5]), fmaxf(z[6], z[7]));
+  float a2 = fmaxf(fmaxf(z[8], z[9]), fmaxf(z[10], z[11]));
+  float a3 = fmaxf(fmaxf(z[12], z[13]), fmaxf(z[14], z[15]));
+  return fmaxf(fmaxf(a0, a1), fmaxf(a2, a3));
+}
+
+__device__ __forceinline__ void decode16(u32x4 a, u32x4 b, float* out) {
+  const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    out[2 * i] = bf16_lo(w[i]);
+    out[2 * i + 1] = bf16_hi(w[i]);
+  }
+}
+
+// Running state of one row over a range of blocks.
+struct DraftLane {
+  float M;        // running max of z
+  double S;       // sum of exp(z - M)
+  CandState cand;
+  u32x4 words;    // Philox block holding the current block's variate
+  __device__ void init() {
+    M = -INFINITY;
+    S = 0.0;
+    cand.init();
+  }
+};
+
+// z[j] = logit of token 32 t + 16 h + j of row (r, k) (-inf at or beyond V);
+// `first` marks the first block of the lane's range (the Philox block of
+// four block words is fetched there and at every fourth block).  Exponentials
+// are taken in base 2 with the scaling folded into one fma.
+__device__ __forceinline__ void draft_block_epilogue(DraftLane& st, const float* z, int r, int k,
+                                                     int t, bool first, uint64_t seed) {
+  if (first || (t & 3) == 0) st.words = noise_block(seed, kStreamDraft, r, k, (uint32_t)t >> 2);
+  const float mt = max_halves(max16(z));
+  if (mt == -INFINITY) return;  // block without mass
+  const float mt2 = mt * kLog2e;
+  float e[16];
+#pragma unroll
+  for (int j = 0; j < 16; ++j) e[j] = __builtin_amdgcn_exp2f(fmaf(z[j], kLog2e, -mt2));
+  const float s = sum_halves(sum16(e));
+  if (mt > st.M) {
+    st.S = st.S * (double)__builtin_amdgcn_exp2f((st.M - mt) * kLog2e) + (double)s;
+    st.M = mt;
+  } else {
+    st.S += (double)(s * __builtin_amdgcn_exp2f((mt - st.M) * kLog2e));
+  }
+  const float sc = fmaf(__builtin_amdgcn_logf(s), kLn2, mt) + gumbel_f32(word_of(st.words, t & 3));
+  const float d = fmaf(kScoreRel, fabsf(mt), kScoreAbs);
+  st.cand.add(sc - d, sc + d, t);
+}
+
+}  // namespace dspark
