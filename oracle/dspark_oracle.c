@@ -571,3 +571,79 @@ ORACLE_API void oracle_threshold_sweep(int64_t R, int64_t gamma, const float* a,
   }
   free(l);
 }
+
+/* ------------------------------------------------------------------------ */
+/* Sequential Temperature Scaling fit.  [P1 §3.2.1]                          */
+/* STS calibrates the cumulative prefix survival on held-out rollouts: a     */
+/* one-dimensional grid search runs left to right, each position's           */
+/* temperature chosen to minimise that position's Expected Calibration Error */
+/* with the earlier positions' temperatures held fixed.                      */
+/* READINGS: rollout n has confidence-head scores s[n, j] (the logit before  */
+/* the sigmoid) and survival labels y[n, j] = 1 iff its draft positions      */
+/* 1..j were all accepted; c = sigmoid(s / T) evaluated in binary64 and      */
+/* rounded to binary32; a_j = fl32(a_{j-1} * c_j), a_0 = 1 (the scheduler's   */
+/* prefix products); ECE over M equal-width bins of [0, 1], bin =            */
+/* min(floor(a M), M - 1): ECE = (1/N) sum_b |sum_{n in b} (y_n - a_n)|,     */
+/* with every a rounded to the nearest multiple of 2^-40 so that the sums    */
+/* are exact integers; the smallest ECE wins, the lowest grid index on ties. */
+/* Outputs: temps[j] = chosen grid value, ece_units[j] = N * ECE at it in    */
+/* units of 2^-40, ece1_units[j] = the same at T = 1 with the earlier         */
+/* positions calibrated, a [N, gamma] the calibrated survival.               */
+/* ------------------------------------------------------------------------ */
+static float sts_conf(double s, double T) { return (float)(1.0 / (1.0 + exp(-s / T))); }
+
+static int64_t sts_units(float a) { return (int64_t)nearbyint(ldexp((double)a, 40)); }
+
+/* N * ECE in units of 2^-40 of survival values a [N] against labels y [N]. */
+ORACLE_API int64_t oracle_ece_units(int64_t N, const float* a, const uint8_t* y, int64_t M) {
+  int64_t* acc = (int64_t*)calloc((size_t)M, sizeof(int64_t));
+  for (int64_t n = 0; n < N; ++n) {
+    int64_t b = (int64_t)floor((double)a[n] * (double)M);
+    if (b > M - 1) b = M - 1;
+    if (b < 0) b = 0;
+    acc[b] += ((int64_t)(y[n] != 0) << 40) - sts_units(a[n]);
+  }
+  int64_t e = 0;
+  for (int64_t b = 0; b < M; ++b) e += acc[b] < 0 ? -acc[b] : acc[b];
+  free(acc);
+  return e;
+}
+
+ORACLE_API void oracle_sts_fit(int64_t N, int64_t gamma, const double* s, const uint8_t* y,
+                               int64_t G, const double* grid, int64_t M, float* temps,
+                               int64_t* ece_units, int64_t* ece1_units, float* a) {
+  float* prev = (float*)malloc((size_t)(N > 0 ? N : 1) * sizeof(float));
+  float* cur = (float*)malloc((size_t)(N > 0 ? N : 1) * sizeof(float));
+  uint8_t* yj = (uint8_t*)malloc((size_t)(N > 0 ? N : 1));
+  for (int64_t n = 0; n < N; ++n) prev[n] = 1.0f;
+  for (int64_t j = 0; j < gamma; ++j) {
+    for (int64_t n = 0; n < N; ++n) yj[n] = y[n * gamma + j];
+    int64_t best = -1, best_e = 0;
+    for (int64_t g = 0; g < G; ++g) {
+      for (int64_t n = 0; n < N; ++n) {
+        volatile float p = prev[n] * sts_conf(s[n * gamma + j], grid[g]);
+        cur[n] = p;
+      }
+      const int64_t e = oracle_ece_units(N, cur, yj, M);
+      if (best < 0 || e < best_e) {
+        best = g;
+        best_e = e;
+      }
+    }
+    for (int64_t n = 0; n < N; ++n) {
+      volatile float p = prev[n] * sts_conf(s[n * gamma + j], 1.0);
+      cur[n] = p;
+    }
+    ece1_units[j] = oracle_ece_units(N, cur, yj, M);
+    temps[j] = (float)grid[best];
+    ece_units[j] = best_e;
+    for (int64_t n = 0; n < N; ++n) {
+      volatile float p = prev[n] * sts_conf(s[n * gamma + j], grid[best]);
+      prev[n] = p;
+      a[n * gamma + j] = p;
+    }
+  }
+  free(prev);
+  free(cur);
+  free(yj);
+}

@@ -106,6 +106,10 @@ def lib() -> ctypes.CDLL:
                                                ctypes.c_double, _i32p]
         L.oracle_conditional_acceptance.argtypes = [ctypes.c_int64, ctypes.c_int64, _u8p,
                                                     _i64p, _i64p]
+        L.oracle_ece_units.argtypes = [ctypes.c_int64, _f32p, _u8p, ctypes.c_int64]
+        L.oracle_ece_units.restype = ctypes.c_int64
+        L.oracle_sts_fit.argtypes = [ctypes.c_int64, ctypes.c_int64, _f64p, _u8p, ctypes.c_int64,
+                                     _f64p, ctypes.c_int64, _f32p, _i64p, _i64p, _f32p]
         L.oracle_threshold_sweep.argtypes = [ctypes.c_int64, ctypes.c_int64, _f32p, _i32p,
                                              ctypes.c_int64, _f64p, _i64p, _i64p]
         _lib = L
@@ -433,3 +437,36 @@ def threshold_sweep(a: np.ndarray, n_accept: np.ndarray, thresholds):
     lib().oracle_threshold_sweep(R, gamma, _p(a, _f32p), _p(na, _i32p), th.size, _p(th, _f64p),
                                  _p(ver, _i64p), _p(acc, _i64p))
     return ver, acc
+
+
+# ---------------------------------------------------------------------------
+# Sequential Temperature Scaling fit  [P1 §3.2.1]
+# ---------------------------------------------------------------------------
+#: ECE sums are exact integers in units of 2^-40 of survival probability
+ECE_UNIT = 2.0 ** -40
+
+
+def ece_units(a: np.ndarray, y: np.ndarray, bins: int) -> int:
+    """N * ECE of survival values a [N] against 0/1 labels y [N], in ECE_UNIT."""
+    a = np.ascontiguousarray(a, dtype=np.float32)
+    y = np.ascontiguousarray(y, dtype=np.uint8)
+    return int(lib().oracle_ece_units(a.size, _p(a, _f32p), _p(y, _u8p), int(bins)))
+
+
+def sts_fit(s: np.ndarray, y: np.ndarray, grid, bins: int = 15):
+    """Left-to-right temperature grid search.  s [N, gamma] scores, y [N, gamma]
+    survival labels, grid [G] candidate temperatures.  Returns temps [gamma],
+    ece [gamma] and ece_at_1 [gamma] (as fractions: units * ECE_UNIT / N), the
+    integer unit values, and the calibrated survival a [N, gamma]."""
+    s = np.ascontiguousarray(s, dtype=np.float64)
+    y = np.ascontiguousarray(y, dtype=np.uint8)
+    grid = np.ascontiguousarray(grid, dtype=np.float64)
+    N, gamma = s.shape
+    temps = np.zeros(gamma, np.float32)
+    eu = np.zeros(gamma, np.int64)
+    e1 = np.zeros(gamma, np.int64)
+    a = np.zeros((N, gamma), np.float32)
+    lib().oracle_sts_fit(N, gamma, _p(s, _f64p), _p(y, _u8p), grid.size, _p(grid, _f64p), int(bins),
+                         _p(temps, _f32p), _p(eu, _i64p), _p(e1, _i64p), _p(a, _f32p))
+    return {"temps": temps, "ece_units": eu, "ece1_units": e1,
+            "ece": eu * ECE_UNIT / max(N, 1), "ece_at_1": e1 * ECE_UNIT / max(N, 1), "a": a}
