@@ -148,8 +148,9 @@ def cpu_baseline(cfg, synth, inp, T, n_req):
 
 def scheduler_variants(cfg, dspark, synth, steps, warmup):
     """Per-call time of the production scheduler (capacity from the round two
-    earlier, top-K on the current round), the static threshold and the
-    acceptance statistics at the workload's R and gamma.  Inputs: seeded
+    earlier, top-K on the current round), the static threshold, the
+    acceptance statistics at the workload's R and gamma, and the STS fit
+    (65,536 rollouts, 53 temperatures, 15 bins).  Inputs: seeded
     confidences; the accept mask follows them (position k accepted with
     probability c_k, until the first rejection)."""
     import torch
@@ -178,22 +179,35 @@ def scheduler_variants(cfg, dspark, synth, steps, warmup):
         dspark.acceptance_stats(dmask, top["a"], dn, thr)
         return cap, top, th
 
+    # STS calibration on 65,536 held-out rollouts: seeded scores, labels from a
+    # model whose acceptance is sigmoid(s / 1.3) at every position
+    n_cal = 65536
+    s_cal = rng.normal(1.5, 1.5, (n_cal, g))
+    y_cal = np.cumprod(rng.random((n_cal, g)) < 1.0 / (1.0 + np.exp(-s_cal / 1.3)), axis=1)
+    ds_cal = torch.from_numpy(s_cal).to(dev)
+    dy_cal = torch.from_numpy(y_cal.astype(np.uint8)).to(dev)
+    grid = torch.from_numpy(np.round(np.linspace(0.4, 3.0, 53), 10)).to(dev)
+
     for _ in range(warmup):
         one()
+        dspark.sts_fit(ds_cal, dy_cal, grid)
     torch.cuda.synchronize()
     dspark.timing_enable(True)
     for _ in range(steps):
         cap, top, th = one()
+        sts = dspark.sts_fit(ds_cal, dy_cal, grid)
     torch.cuda.synchronize()
     dspark.timing_enable(False)
     kern = dspark.timing_report()
     return {"metric": "scheduler variants: microseconds per call", "unit": "us",
             "higher_is_better": False, "n_gpus": 1, "steps": steps, "data": "synthetic",
-            "config": {"workload": cfg.name, "R": R, "gamma": g, "n_thresholds": 64},
+            "config": {"workload": cfg.name, "R": R, "gamma": g, "n_thresholds": 64,
+                       "sts": {"rollouts": n_cal, "grid": 53, "bins": 15}},
             "kernels_us": {k: round(ms * 1e3 / n, 2) for k, (n, ms) in kern.items()},
             "capacity_K": int(cap["K"].cpu()[0]),
             "topk_B": float(top["stats"][0].cpu()),
-            "threshold_mean_length": float(th["lengths"].float().mean().cpu())}
+            "threshold_mean_length": float(th["lengths"].float().mean().cpu()),
+            "sts_temps": [round(float(t), 3) for t in sts["temps"].cpu()]}
 
 
 def main():

@@ -619,4 +619,36 @@ __attribute__((visibility("default"))) int dspark_acceptance_stats(
   return ok();
 }
 
+__attribute__((visibility("default"))) size_t dspark_sts_workspace_bytes(int32_t N, int32_t gamma,
+                                                                        int32_t G, int32_t bins) {
+  if (N < 1 || N > (1 << 20) || gamma < 1 || gamma > 64 || G < 1 || G > kStsMaxGrid || bins < 1 ||
+      bins > kStsMaxBins)
+    return 0;
+  return sts_workspace_bytes(gamma, G, bins);
+}
+
+__attribute__((visibility("default"))) int dspark_sts_fit(int32_t N, int32_t gamma, const double* s,
+                                                          const uint8_t* y, int32_t G,
+                                                          const double* grid, int32_t bins,
+                                                          float* temps, int64_t* ece_units,
+                                                          int64_t* ece1_units, float* a, void* ws,
+                                                          size_t ws_bytes, void* stream) {
+  if (N < 1 || N > (1 << 20) || gamma < 1 || gamma > 64)
+    return fail(DSPARK_ERR_SHAPE, "N=%d, gamma=%d outside [1, 2^20] x [1, 64]", N, gamma);
+  if (G < 1 || G > kStsMaxGrid || bins < 1 || bins > kStsMaxBins)
+    return fail(DSPARK_ERR_SHAPE, "G=%d, bins=%d outside [1, %d] x [1, %d]", G, bins, kStsMaxGrid,
+                kStsMaxBins);
+  if (!s || !y || !grid || !temps || !ece_units || !ece1_units || !a)
+    return fail(DSPARK_ERR_ARG, "sts_fit: tensor pointers must be non-NULL");
+  const size_t need = sts_workspace_bytes(gamma, G, bins);
+  if (!ws) return fail(DSPARK_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", need);
+  if ((uintptr_t)ws % kAlign) return fail(DSPARK_ERR_WORKSPACE, "workspace not %zu-byte aligned", kAlign);
+  if (ws_bytes < need)
+    return fail(DSPARK_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", ws_bytes, need);
+  hipError_t e = launch_sts_fit(N, gamma, s, y, G, grid, bins, temps, ece_units, ece1_units, a, ws,
+                                (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "sts_fit");
+  return ok();
+}
+
 }  // extern "C"

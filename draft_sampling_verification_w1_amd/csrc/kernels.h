@@ -213,6 +213,14 @@ hipError_t launch_schedule_topk(int R, int gamma, const float* c, const int32_t*
                                 const float* sps, float* a, int32_t* lengths, double* stats,
                                 hipStream_t stream);
 
+// ---- Sequential Temperature Scaling fit -------------------------------------
+constexpr int kStsMaxBins = 64;
+constexpr int kStsMaxGrid = 1024;
+size_t sts_workspace_bytes(int gamma, int G, int bins);
+hipError_t launch_sts_fit(int N, int gamma, const double* s, const uint8_t* y, int G,
+                          const double* grid, int bins, float* temps, int64_t* ece_units,
+                          int64_t* ece1_units, float* a, void* ws, hipStream_t stream);
+
 // ---- static threshold and acceptance statistics ---------------------------
 constexpr int kMaxThresholds = 1024;
 hipError_t launch_threshold(int R, int gamma, const float* c, double theta, float* a,

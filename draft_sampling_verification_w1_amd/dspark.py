@@ -21,7 +21,8 @@ _DTYPES = {torch.float32: F32, torch.bfloat16: BF16}
 SYMBOLS = ("dspark_w2_packed_bytes", "dspark_pack_w2", "dspark_workspace_bytes",
            "dspark_draft_step", "dspark_verify", "dspark_confidence", "dspark_schedule",
            "dspark_schedule_capacity", "dspark_schedule_topk", "dspark_schedule_threshold",
-           "dspark_acceptance_stats", "dspark_last_error", "dspark_timing_enable",
+           "dspark_acceptance_stats", "dspark_sts_workspace_bytes", "dspark_sts_fit",
+           "dspark_last_error", "dspark_timing_enable",
            "dspark_timing_report")
 
 
@@ -68,12 +69,16 @@ def lib() -> ctypes.CDLL:
                                                 ctypes.c_double, _vp, _vp, _vp]
         L.dspark_acceptance_stats.argtypes = [ctypes.c_int32, ctypes.c_int32, _vp, _vp, _vp, _vp,
                                               ctypes.c_int32, _vp, _vp, _vp, _vp, _vp]
+        L.dspark_sts_workspace_bytes.argtypes = [ctypes.c_int32] * 4
+        L.dspark_sts_workspace_bytes.restype = ctypes.c_size_t
+        L.dspark_sts_fit.argtypes = [ctypes.c_int32, ctypes.c_int32, _vp, _vp, ctypes.c_int32, _vp,
+                                     ctypes.c_int32, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
         L.dspark_last_error.restype = ctypes.c_char_p
         L.dspark_timing_enable.argtypes = [ctypes.c_int]
         L.dspark_timing_report.argtypes = [ctypes.c_char_p, ctypes.c_size_t]
         for name in ("dspark_pack_w2", "dspark_draft_step", "dspark_verify", "dspark_confidence",
                      "dspark_schedule", "dspark_schedule_capacity", "dspark_schedule_topk",
-                     "dspark_schedule_threshold", "dspark_acceptance_stats",
+                     "dspark_schedule_threshold", "dspark_acceptance_stats", "dspark_sts_fit",
                      "dspark_timing_enable", "dspark_timing_report"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
@@ -326,4 +331,27 @@ def acceptance_stats(accept_mask=None, a=None, n_accept=None, thresholds=None):
                                          _ptr(out.get("accepted")),
                                          _ptr(out.get("sweep_verified")),
                                          _ptr(out.get("sweep_accepted")), _stream()))
+    return out
+
+
+def sts_fit(s, y, grid, bins: int = 15):
+    """Sequential Temperature Scaling fit (dspark_sts_fit).  s [N, gamma] fp64
+    scores, y [N, gamma] uint8 survival labels, grid [G] fp64 temperatures."""
+    N, gamma = s.shape
+    _need(s, "s", dtype=torch.float64)
+    _need(y, "y", dtype=torch.uint8, shape=(N, gamma))
+    _need(grid, "grid", dtype=torch.float64)
+    G = grid.numel()
+    need = lib().dspark_sts_workspace_bytes(N, gamma, G, bins)
+    if need == 0:
+        raise DsparkError(-2, f"bad STS sizes N={N} gamma={gamma} G={G} bins={bins}")
+    dev = s.device
+    ws = torch.empty(need, dtype=torch.uint8, device=dev)
+    out = {"temps": torch.empty(gamma, dtype=torch.float32, device=dev),
+           "ece_units": torch.empty(gamma, dtype=torch.int64, device=dev),
+           "ece1_units": torch.empty(gamma, dtype=torch.int64, device=dev),
+           "a": torch.empty((N, gamma), dtype=torch.float32, device=dev)}
+    _check(lib().dspark_sts_fit(N, gamma, _ptr(s), _ptr(y), G, _ptr(grid), bins, _ptr(out["temps"]),
+                                _ptr(out["ece_units"]), _ptr(out["ece1_units"]), _ptr(out["a"]),
+                                _ptr(ws), need, _stream()))
     return out

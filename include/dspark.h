@@ -196,6 +196,29 @@ int dspark_acceptance_stats(int32_t R, int32_t gamma, const uint8_t* accept_mask
                             int64_t* reached, int64_t* accepted, int64_t* sweep_verified,
                             int64_t* sweep_accepted, void* stream);
 
+/* Sequential Temperature Scaling fit.  [P1 §3.2.1]
+ * Calibrates the prefix survival on N held-out rollouts by a left-to-right
+ * grid search: for j = 1..gamma, with the temperatures of positions < j fixed,
+ *   a_j(T) = fl32(a_{j-1} * fl32(1 / (1 + exp(-s[n,j-1] / T)))) (binary64
+ *            sigmoid rounded to binary32; a_0 = 1),
+ *   N * ECE_j(T) = sum over bins b of |sum_{n in b} (y[n,j-1] - a_j(T))|, bins
+ *            = min(floor(a * bins), bins - 1) over [0, 1], every a rounded to
+ *            the nearest multiple of 2^-40 (exact integer sums),
+ * and T_j = the grid value with the smallest ECE (lowest index on ties).
+ * s: [N, gamma] float64 confidence-head scores (the logit before the sigmoid);
+ * y: [N, gamma] uint8 survival labels (1 iff positions 1..j were all
+ * accepted); grid: [G] float64 candidate temperatures (> 0).
+ * Outputs: temps [gamma] float32 (T_j); ece_units, ece1_units [gamma] int64:
+ * N * ECE in units of 2^-40 at T_j and at T = 1 (earlier positions
+ * calibrated); a [N, gamma] float32, the calibrated survival.
+ * ws: dspark_sts_workspace_bytes(N, gamma, G, bins) bytes, 256-byte aligned
+ * (0 = bad sizes).  Limits: 1 <= N <= 2^20, 1 <= gamma <= 64, 1 <= G <= 1024,
+ * 1 <= bins <= 64.  3 * gamma + 1 launches. */
+size_t dspark_sts_workspace_bytes(int32_t N, int32_t gamma, int32_t G, int32_t bins);
+int dspark_sts_fit(int32_t N, int32_t gamma, const double* s, const uint8_t* y, int32_t G,
+                   const double* grid, int32_t bins, float* temps, int64_t* ece_units,
+                   int64_t* ece1_units, float* a, void* ws, size_t ws_bytes, void* stream);
+
 /* Message for the last failing call on this thread ("" if none). */
 const char* dspark_last_error(void);
 

@@ -126,3 +126,17 @@ def test_production_and_threshold_validation(L):
     assert lib.dspark_acceptance_stats(4, 8, fake, None, None, None, 1025, fake, fake, fake, fake, None) == -2
     assert lib.dspark_acceptance_stats(4, 8, fake, None, None, fake, 3, fake, fake, fake, fake, None) == -1
     assert b"sweep" in lib.dspark_last_error()
+
+
+def test_sts_validation(L):
+    lib = L.lib()
+    fake = ctypes.c_void_p(0x1000)
+    assert lib.dspark_sts_workspace_bytes(0, 4, 8, 15) == 0
+    assert lib.dspark_sts_workspace_bytes(10, 4, 1025, 15) == 0
+    assert lib.dspark_sts_workspace_bytes(10, 4, 8, 65) == 0
+    need = lib.dspark_sts_workspace_bytes(10, 4, 8, 15)
+    assert need >= 4 * 9 * 15 * 8
+    assert lib.dspark_sts_fit(10, 65, fake, fake, 8, fake, 15, fake, fake, fake, fake, fake, need, None) == -2
+    assert lib.dspark_sts_fit(10, 4, fake, None, 8, fake, 15, fake, fake, fake, fake, fake, need, None) == -1
+    assert lib.dspark_sts_fit(10, 4, fake, fake, 8, fake, 15, fake, fake, fake, fake, None, need, None) == -4
+    assert lib.dspark_sts_fit(10, 4, fake, fake, 8, fake, 15, fake, fake, fake, fake, fake, need - 1, None) == -4
