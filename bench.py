@@ -99,6 +99,68 @@ def measured_traffic(kernel):
         return None
 
 
+# bench kernel name -> (pattern of its demangled name, source file)
+KERNELS = {
+    "draft_bias": ("k_bias_bf16<0, 2, true>", "csrc/bias_pass.hip"),
+    "cstar_bias": ("k_bias_bf16<1, 2, true>", "csrc/bias_pass.hip"),
+    "residual_bias": ("k_bias_bf16<2, 2, true>", "csrc/bias_pass.hip"),
+    "target_lse": ("k_target_lse<unsigned short>", "csrc/verify_aux.hip"),
+    "decide": ("k_decide<unsigned short>", "csrc/verify_aux.hip"),
+    "bonus": ("k_bonus<unsigned short>", "csrc/verify_aux.hip"),
+    "finalize": ("k_finalize", "csrc/verify_aux.hip"),
+    "draft_select": ("k_select<0>", "csrc/select.hip"),
+    "residual_select": ("k_select<1>", "csrc/select.hip"),
+    "bonus_select": ("k_select<2>", "csrc/select.hip"),
+    "schedule": ("k_schedule<4, 0>", "csrc/schedule.hip"),
+}
+
+
+def write_traffic(fetch_csv, write_csv, copy_mib, commands):
+    """profiles/traffic.json from two rocprofv3 --pmc runs (FETCH_SIZE, then
+    WRITE_SIZE, KiB per dispatch) of `bench.py --calibrate-copy copy_mib`: each
+    counter is scaled by what it reads for the three plain copies of copy_mib
+    MiB, and each kernel keyed by the hash of its source (stale once the
+    source changes).  Prints the per-kernel table."""
+    import csv
+    pkg = "draft_sampling_verification_w1_amd"
+
+    def load(path):
+        per = {}
+        with open(path) as f:
+            for row in csv.DictReader(f):
+                per.setdefault(row["Kernel_Name"], []).append(float(row["Counter_Value"]))
+        return per
+
+    fetch, write = load(fetch_csv), load(write_csv)
+    copy_bytes = 3 * copy_mib * 2 ** 20
+    fetch_scale = copy_bytes / (sum(fetch["__amd_rocclr_copyBuffer"]) * 1024)
+    write_scale = copy_bytes / (sum(write["__amd_rocclr_copyBuffer"]) * 1024)
+    out = {"command_fetch": commands[0], "command_write": commands[1],
+           "fetch_scale": fetch_scale, "write_scale": write_scale, "kernels": {}}
+    print("| kernel | dispatches | FETCH_SIZE KiB/dispatch | WRITE_SIZE KiB/dispatch | "
+          "scaled MB read | scaled MB written |")
+    print("|---|---|---|---|---|---|")
+    for name, (pat, src) in KERNELS.items():
+        fk = [k for k in fetch if pat in k]
+        wk = [k for k in write if pat in k]
+        if not fk or not wk:
+            continue
+        fv, wv = fetch[fk[0]], write[wk[0]]
+        rd = sum(fv) / len(fv) * 1024 * fetch_scale
+        wr = sum(wv) / len(wv) * 1024 * write_scale
+        path = f"{pkg}/{src}"
+        with open(os.path.join(HERE, path), "rb") as f:
+            sha = hashlib.sha256(f.read()).hexdigest()
+        out["kernels"][name] = {"source": path, "source_sha256": sha,
+                                "bytes_per_launch": int(rd + wr), "read_bytes": int(rd),
+                                "write_bytes": int(wr)}
+        print(f"| {name} (`{pat}`) | {len(fv)} | {sum(fv) / len(fv):.1f} | {sum(wv) / len(wv):.1f} | "
+              f"{rd / 1e6:.2f} | {wr / 1e6:.2f} |")
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(out, f, indent=1)
+    print(f"fetch scale {fetch_scale:.4f}, write scale {write_scale:.4f}; wrote {TRAFFIC_FILE}")
+
+
 def calibrate_copy(mb):
     """A plain device copy of `mb` MiB (the reference kernel for the traffic counters)."""
     import torch
@@ -221,10 +283,21 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="first run a plain device copy of MIB MiB (counter calibration)")
+    ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="no GPU: build profiles/traffic.json from the two counter runs "
+                         "(rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE of this script with "
+                         "--calibrate-copy 1024)")
     ap.add_argument("--scheduler-variants", action="store_true",
                     help="time the production scheduler, static threshold and acceptance "
                          "statistics instead of the round (one JSON line of its own)")
     args = ap.parse_args()
+    if args.write_traffic:
+        cmd = ("cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc {c} --output-format csv -d "
+               "$REPO/gpurun_out/prof/{d} -o bench -- python3 $REPO/bench.py --steps 2 --warmup 1 "
+               "--no-cpu-baseline --calibrate-copy 1024")
+        write_traffic(args.write_traffic[0], args.write_traffic[1], 1024,
+                      (cmd.format(c="FETCH_SIZE", d="fetch"), cmd.format(c="WRITE_SIZE", d="write")))
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               "(the hot path shards over requests with no exchange except one all-gather "
