@@ -272,6 +272,101 @@ def scheduler_variants(cfg, dspark, synth, steps, warmup):
             "sts_temps": [round(float(t), 3) for t in sts["temps"].cpu()]}
 
 
+def decode_rounds(cfg, dspark, synth, rounds, warmup):
+    """Multi-round decoding at the workload's shape: each round's anchors are
+    the previous round's last emitted token (handed over on the device), its
+    Philox key carries the round index.  Per round: fresh synthetic backbone
+    logits (the workload's recipe, generated on the GPU with torch), the
+    draft, synthetic target logits built from the drafted tokens (the
+    workload's recipe: draft logits + noise), then verify of every position
+    and Algorithm 1 on c*.  Input construction is outside the timed calls;
+    T_draft and T_verify are each bracketed by device synchronisation."""
+    import torch
+    from draft_sampling_verification_w1_amd.decode import DecodeLoop
+    R, g, V = cfg.R, cfg.gamma, cfg.V
+    dev = torch.device("cuda:0")
+    tdt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+    W1n, W2n = synth.weights(cfg)
+
+    def to_dev(a):
+        if a.dtype == np.uint16:
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    W1, W2 = to_dev(W1n), to_dev(W2n)
+    W1f, W2f = W1.float(), W2.float()
+    W2p = dspark.pack_w2(W2, V)
+    sps = torch.from_numpy(synth.sps_table(cfg)).to(dev)
+    loop = DecodeLoop(W1, W2p, to_dev(synth.anchors(cfg)), cfg.seed, g, sps=sps)
+    sig = torch.tensor([cfg.noise_sigma(k) for k in range(1, g + 2)], dtype=torch.float32, device=dev)
+    gen = torch.Generator(device=dev)
+    zrng = np.random.default_rng(cfg.seed)
+    state = {}
+
+    def backbone(t):
+        gen.manual_seed(cfg.seed * 100003 + t)
+        U = torch.randn((R, g + 1, V), generator=gen, device=dev) * cfg.u_sigma
+        if cfg.zipf_boost:
+            p = np.arange(1, V + 1, dtype=np.float64) ** -1.1
+            ids = np.searchsorted(np.cumsum(p) / p.sum(), zrng.random(R * (g + 1)), side="right")
+            U.view(-1, V)[torch.arange(R * (g + 1), device=dev),
+                          torch.from_numpy(ids.clip(0, V - 1)).to(dev)] += cfg.zipf_boost
+        state["Ub"] = U[:, g].to(tdt)
+        return U[:, :g].to(tdt).contiguous()
+
+    def target(t, tok):
+        U = state["U"].float()
+        if cfg.target_from_draft:
+            prev = torch.cat([state["anchors"].long()[:, None], tok[:, :-1].long()], dim=1)
+            base = U + (W1f[prev.reshape(-1)] @ W2f).view(R, g, V)
+        else:
+            base = U
+        T = torch.empty((R, g + 1, V), dtype=tdt, device=dev)
+        T[:, :g] = (base + torch.randn((R, g, V), generator=gen, device=dev) * sig[:g, None]).to(tdt)
+        T[:, g] = (state["Ub"].float() + torch.randn((R, V), generator=gen, device=dev) * sig[g]).to(tdt)
+        return T
+
+    out = []
+    for t in range(warmup + rounds):
+        state["U"] = backbone(t)
+        state["anchors"] = loop.anchors.clone()
+        times = {}
+
+        def target_timed(tt, tok):
+            torch.cuda.synchronize()
+            times["draft"] = time.perf_counter() - times["t0"]
+            T = target(tt, tok)
+            torch.cuda.synchronize()
+            times["t1"] = time.perf_counter()
+            return T
+
+        torch.cuda.synchronize()
+        times["t0"] = time.perf_counter()
+        r = loop.round(state["U"], target_timed)
+        torch.cuda.synchronize()
+        t_verify = time.perf_counter() - times["t1"]
+        if t < warmup:
+            continue
+        n_acc = r["n_accept"].cpu().numpy()
+        a = r["a"].cpu().numpy().astype(np.float64)
+        tau = float((n_acc + 1).mean())
+        pred = float((1.0 + a.sum(axis=1)).mean())   # expected tau with every position verified
+        ms = (times["draft"] + t_verify) * 1e3
+        out.append({"round": t - warmup, "tau": round(tau, 3), "tau_from_cstar": round(pred, 3),
+                    "ms_draft": round(times["draft"] * 1e3, 3), "ms_verify": round(t_verify * 1e3, 3),
+                    "L_us_per_token": round(ms * 1e3 / tau, 2),
+                    "alg1_lengths_mean": round(float(r["lengths"].float().mean().cpu()), 3)})
+    tau = np.mean([o["tau"] for o in out])
+    ms = np.mean([o["ms_draft"] + o["ms_verify"] for o in out])
+    return {"metric": "multi-round decoding: tau per round and L = (T_draft + T_verify) / tau",
+            "unit": "us per token", "value": round(ms * 1e3 / tau, 2), "higher_is_better": False,
+            "n_gpus": 1, "rounds": rounds, "warmup": warmup, "data": "synthetic",
+            "config": {"workload": cfg.name, "R": R, "gamma": g, "V": V},
+            "mean_tau": round(float(tau), 3),
+            "mean_tau_from_cstar": round(float(np.mean([o["tau_from_cstar"] for o in out])), 3),
+            "mean_ms_per_round": round(float(ms), 3), "per_round": out}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -287,6 +382,8 @@ def main():
                     help="no GPU: build profiles/traffic.json from the two counter runs "
                          "(rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE of this script with "
                          "--calibrate-copy 1024)")
+    ap.add_argument("--rounds", type=int, default=0,
+                    help="run this many rounds of multi-round decoding instead (one JSON line)")
     ap.add_argument("--scheduler-variants", action="store_true",
                     help="time the production scheduler, static threshold and acceptance "
                          "statistics instead of the round (one JSON line of its own)")
@@ -315,6 +412,9 @@ def main():
         calibrate_copy(args.calibrate_copy)
     if args.scheduler_variants:
         print(json.dumps(scheduler_variants(cfg, dspark, synth, args.steps, args.warmup)), flush=True)
+        return
+    if args.rounds:
+        print(json.dumps(decode_rounds(cfg, dspark, synth, args.rounds, args.warmup)), flush=True)
         return
     tdt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
 

@@ -470,3 +470,31 @@ def sts_fit(s: np.ndarray, y: np.ndarray, grid, bins: int = 15):
                          _p(temps, _f32p), _p(eu, _i64p), _p(e1, _i64p), _p(a, _f32p))
     return {"temps": temps, "ece_units": eu, "ece1_units": e1,
             "ece": eu * ECE_UNIT / max(N, 1), "ece_at_1": e1 * ECE_UNIT / max(N, 1), "a": a}
+
+
+# ---------------------------------------------------------------------------
+# multi-round decoding  [P1 §요약, §3, §3.1]
+# ---------------------------------------------------------------------------
+def round_key(seed: int, t: int) -> int:
+    """READING: round t draws with the Philox key seed + t * 2^32 (mod 2^64)."""
+    return (int(seed) + (int(t) << 32)) % (1 << 64)
+
+
+def decode_rounds(W1, W2, anchors, seed: int, rounds: int, backbone, target):
+    """Rounds of draft + verify of every position: round t drafts from the
+    anchors with U = backbone(t), takes T = target(t, U, anchors, tokens) and emits the
+    accepted prefix plus the corrective or bonus token, which is the next
+    round's anchor.  Returns one dict per round (draft and verify outputs, the
+    round's anchors and key)."""
+    out = []
+    anchors = np.asarray(anchors, np.int32).copy()
+    for t in range(rounds):
+        key = round_key(seed, t)
+        U = backbone(t)
+        d = draft(U, W1, W2, anchors, key)
+        T = target(t, U, anchors, d["tokens"])
+        v = verify(U, W1, W2, anchors, d["tokens"], T, None, key)
+        out.append({"anchors": anchors.copy(), "key": key, "U": U, "T": T, "draft": d,
+                    "verify": v})
+        anchors = v["out_token"].astype(np.int32).copy()
+    return out
