@@ -190,7 +190,8 @@ int dspark_schedule_threshold(int32_t R, int32_t gamma, const float* c, double t
  * gamma positions, thresholds [n_thr] float64): sweep_verified[g] = sum_r
  * l_r(thresholds[g]) with l_r as in dspark_schedule_threshold, and
  * sweep_accepted[g] = sum_r min(n_accept[r], l_r) -- the tokens a verify
- * limited by that threshold checks and accepts.  One workgroup; no workspace. */
+ * limited by that threshold checks and accepts.  One workgroup for the mask and
+ * one per threshold; no workspace. */
 int dspark_acceptance_stats(int32_t R, int32_t gamma, const uint8_t* accept_mask, const float* a,
                             const int32_t* n_accept, const double* thresholds, int32_t n_thr,
                             int64_t* reached, int64_t* accepted, int64_t* sweep_verified,
