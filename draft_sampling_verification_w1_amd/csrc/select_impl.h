@@ -337,16 +337,25 @@ __device__ void select_row(const SelectArgs& a, int bf16_flag, int i, SelShared&
         double m = w;
 #pragma unroll
         for (int off = 1; off < 32; off <<= 1) m = fmax(m, __shfl_xor(m, off, 64));
-        double s = (m > -INFINITY) ? exp(w - m) : 0.0;
-#pragma unroll
-        for (int off = 1; off < 32; off <<= 1) s += __shfl_xor(s, off, 64);
-        if (m > -INFINITY) {
-          const double sc = m + log(s) + gumbel_at(a.seed, sblock, q.r, q.k, (uint32_t)blk);
-          if (bb < 0 || sc > best || (sc == best && blk < bb)) {
-            best = sc;
+        if (total == 1) {
+          // the only block that can win: its score decides nothing
+          if (m > -INFINITY) {
             bb = blk;
             sh.zb[tid] = w;
             sh.gb[tid] = sh.gc[tid];
+          }
+        } else {
+          double s = (m > -INFINITY) ? exp(w - m) : 0.0;
+#pragma unroll
+          for (int off = 1; off < 32; off <<= 1) s += __shfl_xor(s, off, 64);
+          if (m > -INFINITY) {
+            const double sc = m + log(s) + gumbel_at(a.seed, sblock, q.r, q.k, (uint32_t)blk);
+            if (bb < 0 || sc > best || (sc == best && blk < bb)) {
+              best = sc;
+              bb = blk;
+              sh.zb[tid] = w;
+              sh.gb[tid] = sh.gc[tid];
+            }
           }
         }
         if (tid == 0) sh.brun = bb;
