@@ -455,6 +455,57 @@ __global__ __launch_bounds__(kThreads) void k_bias_f32(const BiasPassArgs a) {
   const f32x4* W2T = reinterpret_cast<const f32x4*>(a.W2p);
   constexpr bool kNeedT = MODE != kModeDraft;
 
+  if (active_rows - row0 <= 32) {
+    // At most one wave's rows: the 8 waves share them and split the rank
+    // instead, wave w summing ranks [32w, 32w + 32); wave 0 adds the eight
+    // partial sums in a fixed order and runs the epilogue.
+    __shared__ float part[kWaves][16][64];
+    const int row = row0 + n;
+    const RowCtx rc = row_ctx(a, row, active_rows, false, a.k);
+    LaneState<MODE> st;
+    st.init();
+    const f32x4* w1 = reinterpret_cast<const f32x4*>(
+        reinterpret_cast<const float*>(a.W1) + (int64_t)rc.prev * kRank);
+    const float* ur = reinterpret_cast<const float*>(rc.urow);
+    const float* tr = reinterpret_cast<const float*>(rc.trow);
+    for (int t = t_begin; t < t_end; ++t) {
+      const int vb = t * kTile + 16 * h;
+      float acc[16];
+#pragma unroll
+      for (int j = 0; j < 16; ++j) acc[j] = 0.f;
+      if (rc.active) {
+        for (int i4 = 8 * wave; i4 < 8 * wave + 8; ++i4) {
+          const f32x4 x = w1[i4];
+#pragma unroll
+          for (int j = 0; j < 16; ++j) {
+            const f32x4 y = W2T[(int64_t)(vb + j) * (kRank / 4) + i4];
+            acc[j] = fmaf(x.x, y.x, acc[j]);
+            acc[j] = fmaf(x.y, y.y, acc[j]);
+            acc[j] = fmaf(x.z, y.z, acc[j]);
+            acc[j] = fmaf(x.w, y.w, acc[j]);
+          }
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < 16; ++j) part[wave][j][lane] = acc[j];
+      __syncthreads();
+      if (wave == 0) {
+        float z[16], tv[16];
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          float b = part[0][j][lane];
+          for (int w = 1; w < kWaves; ++w) b += part[w][j][lane];
+          z[j] = (rc.active && vb + j < a.V) ? ur[vb + j] + b : -INFINITY;
+          tv[j] = (kNeedT && rc.active && vb + j < a.V) ? tr[vb + j] : -INFINITY;
+        }
+        epilogue<MODE>(st, z, tv, rc, t, t == t_begin, a.seed);
+      }
+      __syncthreads();
+    }
+    if (wave == 0) finish<MODE>(st, rc, row, split, a, h == 0);
+    return;
+  }
+
   const int row = row0 + wave * 32 + n;
   const RowCtx rc = row_ctx(a, row, active_rows, false, a.k);
   LaneState<MODE> st;
