@@ -101,9 +101,9 @@ def measured_traffic(kernel):
 
 # bench kernel name -> (pattern of its demangled name, source file)
 KERNELS = {
-    "draft_bias": ("k_bias_bf16<0, 2, true>", "csrc/bias_pass.hip"),
-    "cstar_bias": ("k_bias_bf16<1, 2, true>", "csrc/bias_pass.hip"),
-    "residual_bias": ("k_bias_bf16<2, 2, true>", "csrc/bias_pass.hip"),
+    "draft_bias": ("k_bias_bf16<0, 2, true, false>", "csrc/bias_pass.hip"),
+    "cstar_bias": ("k_bias_bf16<1, 2, true, false>", "csrc/bias_pass.hip"),
+    "residual_bias": ("k_bias_bf16<2, 2, true, false>", "csrc/bias_pass.hip"),
     "target_lse": ("k_target_lse<unsigned short>", "csrc/verify_aux.hip"),
     "decide": ("k_decide<unsigned short>", "csrc/verify_aux.hip"),
     "bonus": ("k_bonus<unsigned short>", "csrc/verify_aux.hip"),
@@ -173,39 +173,73 @@ def calibrate_copy(mb):
     log(f"[bench] copy calibration: 3 copies of {mb} MiB")
 
 
-def cpu_baseline(cfg, synth, inp, T, n_req):
-    """The oracle (fp64 CPU) on the first n_req requests of the same workload:
-    the same step as the GPU's (draft, verify of every position, schedule on c*;
+def cpu_model():
+    """The host CPU's model name (first 'model name' of /proc/cpuinfo)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(cfg, synth, inp, T, n_req, n_req_1t, runs=3):
+    """The oracle (fp64 CPU) on the first requests of the same workload: the
+    same step as the GPU's (draft, verify of every position, schedule on c*;
     with a confidence head: draft, confidence, schedule, verify of the
-    scheduled lengths -- on a sample the scheduler sees the sample's requests only)."""
+    scheduled lengths -- on a sample the scheduler sees the sample's requests
+    only).  Median of `runs` runs on all the host's threads over n_req
+    requests, and the same at one thread over n_req_1t requests."""
+    from threadpoolctl import threadpool_limits
     from oracle import oracle as O
-    req = list(range(n_req))
-    U = inp["U"][:n_req]
-    anchors = inp["anchors"][:n_req]
     sps = synth.sps_table(cfg)
     scheduled = cfg.confidence_H > 0
     if scheduled:
-        h, w = synth.confidence_inputs(cfg, requests=req)
+        h_all, w = synth.confidence_inputs(cfg, requests=range(max(n_req, n_req_1t)))
         temps = synth.sts_temperatures(cfg)
-    t0 = time.perf_counter()
-    od = O.draft(U, inp["W1"], inp["W2"], anchors, cfg.seed)
-    if scheduled:
-        c = O.confidence(h, w, temps, inp["W1"], anchors, od["tokens"])
-        lengths = O.schedule(O.prefix_products(c), sps)["lengths"]
-        O.verify(U, inp["W1"], inp["W2"], anchors, od["tokens"], T[:n_req], lengths, cfg.seed,
-                 requests=req)
-    else:
-        ov = O.verify(U, inp["W1"], inp["W2"], anchors, od["tokens"], T[:n_req], None, cfg.seed,
-                      requests=req)
-        O.schedule(O.prefix_products(np.nan_to_num(ov["cstar"], nan=0.0).astype(np.float32)), sps)
-    dt = time.perf_counter() - t0
-    cores = int(os.environ.get("OMP_NUM_THREADS") or os.cpu_count())
-    what = "the whole batch" if n_req == cfg.R else f"the first {n_req} of {cfg.R} requests"
+
+    def one(n):
+        req = list(range(n))
+        U, anchors = inp["U"][:n], inp["anchors"][:n]
+        t0 = time.perf_counter()
+        od = O.draft(U, inp["W1"], inp["W2"], anchors, cfg.seed)
+        if scheduled:
+            c = O.confidence(h_all[:n], w, temps, inp["W1"], anchors, od["tokens"])
+            lengths = O.schedule(O.prefix_products(c), sps)["lengths"]
+            O.verify(U, inp["W1"], inp["W2"], anchors, od["tokens"], T[:n], lengths, cfg.seed,
+                     requests=req)
+        else:
+            ov = O.verify(U, inp["W1"], inp["W2"], anchors, od["tokens"], T[:n], None, cfg.seed,
+                          requests=req)
+            O.schedule(O.prefix_products(np.nan_to_num(ov["cstar"], nan=0.0).astype(np.float32)), sps)
+        return time.perf_counter() - t0
+
+    threads = int(os.environ.get("OMP_NUM_THREADS") or os.cpu_count())
+    out = {}
+    for label, n, nt in (("all", n_req, threads), ("one", n_req_1t, 1)):
+        O.set_threads(nt)
+        with threadpool_limits(limits=nt):
+            times = sorted(one(n) for _ in range(runs))
+        out[label] = (n, nt, times[len(times) // 2], times)
+        log(f"[bench] oracle on {n} requests at {nt} thread(s): " +
+            ", ".join(f"{t:.2f}s" for t in times))
+    O.set_threads(threads)
+    n, nt, med, times = out["all"]
+    n1, _, med1, times1 = out["one"]
     steps = ("draft + confidence + schedule + verify(scheduled lengths)" if scheduled
              else "draft + verify + schedule")
-    return {"value": round(n_req * cfg.gamma / dt, 2), "unit": "positions/s", "cores": cores,
-            "kind": "oracle",
-            "sample": f"{what} ({n_req * cfg.gamma} positions): oracle {steps} in fp64, {dt:.1f} s"}
+    what = "the whole batch" if n == cfg.R else f"the first {n} of {cfg.R} requests"
+    return {"value": round(n * cfg.gamma / med, 2), "unit": "positions/s", "cores": nt,
+            "kind": "oracle", "cpu_model": cpu_model(),
+            "sample": (f"{what} ({n * cfg.gamma} positions): oracle {steps} in fp64 at {nt} threads, "
+                       f"median of {runs} runs ({', '.join(f'{t:.2f}' for t in times)} s)"),
+            "single_thread": {"value": round(n1 * cfg.gamma / med1, 2), "unit": "positions/s",
+                              "cores": 1,
+                              "sample": (f"the first {n1} of {cfg.R} requests ({n1 * cfg.gamma} "
+                                         f"positions) at 1 thread, median of {runs} runs "
+                                         f"({', '.join(f'{t:.2f}' for t in times1)} s)")}}
 
 
 def scheduler_variants(cfg, dspark, synth, steps, warmup):
@@ -374,7 +408,11 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="high_concurrency")
     ap.add_argument("--cpu-requests", type=int, default=0,
-                    help="requests in the CPU oracle's sample (default: the whole batch)")
+                    help="requests in the CPU oracle's all-thread sample (default: the whole batch)")
+    ap.add_argument("--cpu-requests-1t", type=int, default=8,
+                    help="requests in the CPU oracle's one-thread sample")
+    ap.add_argument("--cold-steps", type=int, default=5,
+                    help="steps timed one by one after streaming 1 GiB through the caches (0: none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="first run a plain device copy of MIB MiB (counter calibration)")
@@ -486,6 +524,26 @@ def main():
     value = positions / elapsed
     log(f"[bench] {args.steps} steps: {ms:.3f} ms/step, {value / 1e6:.3f} M positions/s")
 
+    # cold: before each step a 512 MiB copy (1 GiB of traffic) evicts the 256 MB
+    # Infinity Cache and the L2s; each step is timed alone with events on the
+    # stream the library launches on (torch's current stream)
+    cold_ms = None
+    if args.cold_steps > 0:
+        src = torch.empty(512 << 20, dtype=torch.uint8, device=dev).fill_(3)
+        dst = torch.empty_like(src)
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(args.cold_steps)]
+        for e0, e1 in ev:
+            dst.copy_(src)
+            e0.record()
+            step()
+            e1.record()
+        torch.cuda.synchronize()
+        cold = sorted(e0.elapsed_time(e1) for e0, e1 in ev)
+        cold_ms = cold[len(cold) // 2]
+        del src, dst
+        log(f"[bench] cold (caches flushed before each step): median {cold_ms:.3f} ms/step")
+
     # the same steps again with per-kernel HIP-event timing on the launch stream
     dspark.timing_enable(True)
     t1 = time.perf_counter()
@@ -536,13 +594,19 @@ def main():
         "profiled_ms_per_step": round(prof_ms, 4),
         "mean_accepted": round(float(n_acc.mean()), 3),
     }
+    if cold_ms is not None:
+        result["cold"] = {"ms_per_step": round(cold_ms, 4),
+                          "positions_per_s": round(R * g / (cold_ms * 1e-3), 1),
+                          "steps": args.cold_steps,
+                          "how": "median of single steps, each after a 512 MiB device copy"}
     if scheduled:
         result["mean_scheduled_length"] = round(float(lengths.mean()), 3)
     if not args.no_cpu_baseline:
         n_cpu = min(args.cpu_requests or R, R)
-        log(f"[bench] CPU oracle on {n_cpu} requests ...")
+        n_1t = min(args.cpu_requests_1t, R)
+        log(f"[bench] CPU oracle on {n_cpu} requests (all threads), {n_1t} (one thread) ...")
         inp = {"U": U, "W1": W1, "W2": W2, "anchors": anchors}
-        result["cpu_baseline"] = cpu_baseline(cfg, synth, inp, T, n_cpu)
+        result["cpu_baseline"] = cpu_baseline(cfg, synth, inp, T, n_cpu, n_1t)
     print(json.dumps(result), flush=True)
 
 

@@ -197,9 +197,10 @@ BlockCands cands_at(void* ws, const CandLayout& L) {
   return c;
 }
 
+// Packed tiles, then one float per tile (max |W2| over the tile).
 size_t packed_bytes(const dspark_problem* p) {
-  const size_t ntiles = ((size_t)p->V + kTile - 1) / kTile;
-  return p->dtype == DSPARK_BF16 ? ntiles * kSteps * 64 * 16 : ntiles * kTile * kRank * 4;
+  const int ntiles = (p->V + kTile - 1) / kTile;
+  return (size_t)w2_tiles_bytes(p->dtype == DSPARK_BF16, ntiles) + (size_t)ntiles * sizeof(float);
 }
 
 // ---- per-kernel timing (tracing) -----------------------------------------
@@ -328,7 +329,7 @@ __attribute__((visibility("default"))) size_t dspark_workspace_bytes(const dspar
 
 __attribute__((visibility("default"))) int dspark_draft_step(
     const dspark_problem* p, const void* U, const void* W1, const void* W2p,
-    const int32_t* anchors, int32_t* tokens, double* lse, double* logq, void* ws,
+    const int32_t* anchors, int32_t* tokens, double* lse, double* logq, float* logpd, void* ws,
     size_t ws_bytes, void* stream) {
   if (int e = check_problem(p)) return e;
   if (!U || !W1 || !W2p || !anchors || !tokens || !lse || !logq)
@@ -357,6 +358,7 @@ __attribute__((visibility("default"))) int dspark_draft_step(
   a.pm = at<float>(ws, L.pm);
   a.ps = at<double>(ws, L.ps);
   a.cand = cands_at(ws, L.cand);
+  a.zout = logpd;
   SelectArgs q = {};
   q.R = p->R;
   q.gamma = p->gamma;
@@ -388,6 +390,10 @@ __attribute__((visibility("default"))) int dspark_draft_step(
     if (e != hipSuccess) return hip_fail(e, "draft pass");
     e = launch_select(kSelDraft, bf16, q, s);
     if (e != hipSuccess) return hip_fail(e, "draft select");
+  }
+  if (logpd) {
+    hipError_t e = launch_logpd(p->R * p->gamma, p->V, lse, logpd, s);
+    if (e != hipSuccess) return hip_fail(e, "draft log p^d");
   }
   return ok();
 }

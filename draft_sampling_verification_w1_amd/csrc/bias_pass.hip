@@ -19,9 +19,11 @@
 // U (and T), placed with an xor swizzle so that the lanes' 16-byte fragment
 // reads hit distinct LDS banks.  The gathered W1 rows of a wave's 32 rows are
 // the B operand, held in registers for the whole pass; v_mfma_f32_32x32x16_bf16
-// accumulates in fp32 on top of the backbone logits.  The packed tile order
+// accumulates in fp32.  The packed tile order
 // makes lane (n, h) own tokens [16h, 16h+16) of row n, so a 32-token block is
-// the lane pair (n, n+32).
+// the lane pair (n, n+32).  The chain accumulates B from zero and the backbone
+// logits are added to its result, so that the binary32 error of z is bounded
+// by the contraction's own magnitude (see kContractErr).
 // Binary32 rows compute the same bias with a VALU dot product.
 #include "device_common.h"
 #include "draft_epilogue.h"
@@ -131,6 +133,16 @@ __device__ __forceinline__ u32x4 gload16(const void* p) {
   return *(global_u32x4*)(p);
 }
 
+// ||W1[x]||_1 of a binary32 row (64 16-byte chunks).
+__device__ __forceinline__ float w1_norm1(const f32x4* w1) {
+  float n1 = 0.f;
+  for (int i = 0; i < kRank / 4; ++i) {
+    const f32x4 x = w1[i];
+    n1 += (fabsf(x.x) + fabsf(x.y)) + (fabsf(x.z) + fabsf(x.w));
+  }
+  return n1;
+}
+
 template <int MODE>
 struct LaneState;
 
@@ -160,11 +172,14 @@ struct LaneState<kModeResidual> {
 // vb + j (j < 16) of one row (block t = its tile) and, in the verify modes, the
 // target logits tv[j]; entries at or beyond V hold -inf.  Exponentials are
 // taken in base 2 with the scaling folded into one fma.
+// dz bounds the binary32 contraction error of every logit of the tile
+// (kContractErr ||W1[x]||_1 max|W2| over the tile).
 template <int MODE>
 __device__ __forceinline__ void epilogue(LaneState<MODE>& st, const float* z, const float* tv,
-                                         const RowCtx& rc, int t, bool first, uint64_t seed) {
+                                         const RowCtx& rc, int t, bool first, uint64_t seed,
+                                         float dz) {
   if constexpr (MODE == kModeDraft) {
-    draft_block_epilogue(st, z, rc.r, rc.k, t, first, seed);
+    draft_block_epilogue(st, z, rc.r, rc.k, t, first, seed, dz);
   } else if constexpr (MODE == kModeCstar) {
     float e[16];
 #pragma unroll
@@ -188,7 +203,7 @@ __device__ __forceinline__ void epilogue(LaneState<MODE>& st, const float* z, co
     const float g = gumbel_f32(word_of(st.words, t & 3));
     constexpr float kG = 0x1p-13f;  // Gumbel and log2 rounding
     st.wpos += W;
-    const float err = rc.eps * P;
+    const float err = (rc.eps + dz) * P;
     if (W + err > 0.f) {
       const float hi = fmaf(__builtin_amdgcn_logf(W + err), kLn2, g) + kG;
       const float lo = (W > err) ? fmaf(__builtin_amdgcn_logf(W - err), kLn2, g) - kG : -INFINITY;
@@ -236,7 +251,8 @@ __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast
 // own area (xor-swizzled 16-byte slots); one barrier per stage publishes the
 // W2 tiles.  VEC: rows 16-byte aligned (vector loads), else scalar loads.
 // One (split, row block) of a pass with `nsplit` splits.
-template <int MODE, int D, bool VEC>
+// ZOUT (draft only): also store every logit z = U + B of the pass to a.zout.
+template <int MODE, int D, bool VEC, bool ZOUT>
 __device__ void bias_body(const BiasPassArgs& a, int split, int nsplit, int row_block,
                           int active_rows, int kpos) {
   constexpr bool kNeedT = MODE != kModeDraft;
@@ -357,6 +373,19 @@ __device__ void bias_body(const BiasPassArgs& a, int split, int nsplit, int row_
     constexpr int kLoadsPerStage = 4 * (kNeedT ? 3 : 2);
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(kLoadsPerStage * (D - 1)));
   }
+  // ||W1[x]||_1 of the lane's row (each half of the wave holds half the rank)
+  float n1 = 0.f;
+#pragma unroll
+  for (int s = 0; s < kSteps; ++s) {
+    const u32x4 v = __builtin_bit_cast(u32x4, bop[s]);
+    n1 += (fabsf(bf16_lo(v.x)) + fabsf(bf16_hi(v.x))) + (fabsf(bf16_lo(v.y)) + fabsf(bf16_hi(v.y))) +
+          (fabsf(bf16_lo(v.z)) + fabsf(bf16_hi(v.z))) + (fabsf(bf16_lo(v.w)) + fabsf(bf16_hi(v.w)));
+  }
+  const float kz = kContractErr * sum_halves(n1);
+  const float* tmax = w2_tile_absmax(a.W2p, true, a.ntiles);
+  float* zrow = nullptr;
+  if constexpr (ZOUT)
+    if (rc.active) zrow = a.zout + ((int64_t)rc.r * a.gamma + (rc.k - 1)) * (int64_t)a.V;
 
   const int sw = seg_swz<NSEG>(n);
   const int c_stop = c_begin + (c_end - c_begin + D - 1) / D * D;
@@ -375,14 +404,13 @@ __device__ void bias_body(const BiasPassArgs& a, int split, int nsplit, int row_
         for (int tau = 0; tau < ST; ++tau) {
           const int t = c * ST + tau;
           if (t < t_end) {
-            // backbone logits seed the accumulator: the MFMA chain yields z = U + B
+            // the chain accumulates B from zero (its error then scales with
+            // sum |W1 W2| only); the backbone logits are added after it
             const int s0 = 4 * tau + 2 * h;
-            float z[16];
-            decode16(*reinterpret_cast<const u32x4*>(ru_lds + ((s0 ^ sw) * 16)),
-                     *reinterpret_cast<const u32x4*>(ru_lds + (((s0 + 1) ^ sw) * 16)), z);
+            const float dz = kz * tmax[t];
             f32x16 acc;
 #pragma unroll
-            for (int j = 0; j < 16; ++j) acc[j] = z[j];
+            for (int j = 0; j < 16; ++j) acc[j] = 0.f;
             const u32x4* At = reinterpret_cast<const u32x4*>(ra_lds + tau * kTileBytesA) + lane;
             if constexpr (kBatchA) {
               // all 16 A fragments in flight before the chain starts (one LDS
@@ -399,13 +427,23 @@ __device__ void bias_body(const BiasPassArgs& a, int split, int nsplit, int row_
               for (int s = 0; s < kSteps; ++s)
                 acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(At[s * 64]), bop[s], acc, 0, 0, 0);
             }
+            float z[16];
+            decode16(*reinterpret_cast<const u32x4*>(ru_lds + ((s0 ^ sw) * 16)),
+                     *reinterpret_cast<const u32x4*>(ru_lds + (((s0 + 1) ^ sw) * 16)), z);
 #pragma unroll
-            for (int j = 0; j < 16; ++j) z[j] = acc[j];
+            for (int j = 0; j < 16; ++j) z[j] += acc[j];
+            if constexpr (ZOUT) {
+              const int vb = t * kTile + 16 * h;
+              if (zrow)
+#pragma unroll
+                for (int j = 0; j < 16; ++j)
+                  if (vb + j < a.V) zrow[vb + j] = z[j];
+            }
             float tv[16];
             if constexpr (kNeedT)
               decode16(*reinterpret_cast<const u32x4*>(rt_lds + ((s0 ^ sw) * 16)),
                        *reinterpret_cast<const u32x4*>(rt_lds + (((s0 + 1) ^ sw) * 16)), tv);
-            epilogue<MODE>(st, z, tv, rc, t, t == t_begin, a.seed);
+            epilogue<MODE>(st, z, tv, rc, t, t == t_begin, a.seed, dz);
           }
         }
       }
@@ -429,11 +467,11 @@ __device__ __forceinline__ PassWork pass_work(const BiasPassArgs& a, int active_
   return {id % ns, ns, id / ns};
 }
 
-template <int MODE, int D, bool VEC>
+template <int MODE, int D, bool VEC, bool ZOUT = false>
 __global__ __launch_bounds__(kThreads) void k_bias_bf16(const BiasPassArgs a) {
   const int active_rows = a.row_count ? min(*a.row_count, a.nrows) : a.nrows;
   const PassWork w = pass_work(a, active_rows);
-  bias_body<MODE, D, VEC>(a, w.split, w.nsplit, w.row_block, active_rows, a.k);
+  bias_body<MODE, D, VEC, ZOUT>(a, w.split, w.nsplit, w.row_block, active_rows, a.k);
 }
 
 // Binary32 rows: same row/lane layout, bias by VALU dot products against the
@@ -453,6 +491,7 @@ __global__ __launch_bounds__(kThreads) void k_bias_f32(const BiasPassArgs a) {
   const int t_begin = split_tile(split, work.nsplit, a.ntiles, a.tiles_per_stage);
   const int t_end = split_tile(split + 1, work.nsplit, a.ntiles, a.tiles_per_stage);
   const f32x4* W2T = reinterpret_cast<const f32x4*>(a.W2p);
+  const float* tmax = w2_tile_absmax(a.W2p, false, a.ntiles);
   constexpr bool kNeedT = MODE != kModeDraft;
 
   if (active_rows - row0 <= 32) {
@@ -468,6 +507,10 @@ __global__ __launch_bounds__(kThreads) void k_bias_f32(const BiasPassArgs a) {
         reinterpret_cast<const float*>(a.W1) + (int64_t)rc.prev * kRank);
     const float* ur = reinterpret_cast<const float*>(rc.urow);
     const float* tr = reinterpret_cast<const float*>(rc.trow);
+    const float kz = kContractErr * (rc.active ? w1_norm1(w1) : 0.f);
+    float* zrow = (MODE == kModeDraft && a.zout && rc.active)
+                      ? a.zout + ((int64_t)rc.r * a.gamma + (rc.k - 1)) * (int64_t)a.V
+                      : nullptr;
     for (int t = t_begin; t < t_end; ++t) {
       const int vb = t * kTile + 16 * h;
       float acc[16];
@@ -497,8 +540,9 @@ __global__ __launch_bounds__(kThreads) void k_bias_f32(const BiasPassArgs a) {
           for (int w = 1; w < kWaves; ++w) b += part[w][j][lane];
           z[j] = (rc.active && vb + j < a.V) ? ur[vb + j] + b : -INFINITY;
           tv[j] = (kNeedT && rc.active && vb + j < a.V) ? tr[vb + j] : -INFINITY;
+          if (zrow && vb + j < a.V) zrow[vb + j] = z[j];
         }
-        epilogue<MODE>(st, z, tv, rc, t, t == t_begin, a.seed);
+        epilogue<MODE>(st, z, tv, rc, t, t == t_begin, a.seed, kz * tmax[t]);
       }
       __syncthreads();
     }
@@ -515,6 +559,10 @@ __global__ __launch_bounds__(kThreads) void k_bias_f32(const BiasPassArgs a) {
         reinterpret_cast<const float*>(a.W1) + (int64_t)rc.prev * kRank);
     const float* ur = reinterpret_cast<const float*>(rc.urow);
     const float* tr = reinterpret_cast<const float*>(rc.trow);
+    const float kz = kContractErr * w1_norm1(w1);
+    float* zrow = (MODE == kModeDraft && a.zout)
+                      ? a.zout + ((int64_t)rc.r * a.gamma + (rc.k - 1)) * (int64_t)a.V
+                      : nullptr;
     for (int t = t_begin; t < t_end; ++t) {
       const int vb = t * kTile + 16 * h;
       float acc[16];
@@ -536,8 +584,9 @@ __global__ __launch_bounds__(kThreads) void k_bias_f32(const BiasPassArgs a) {
       for (int j = 0; j < 16; ++j) {
         z[j] = (vb + j < a.V) ? ur[vb + j] + acc[j] : -INFINITY;
         tv[j] = (kNeedT && vb + j < a.V) ? tr[vb + j] : -INFINITY;
+        if (zrow && vb + j < a.V) zrow[vb + j] = z[j];
       }
-      epilogue<MODE>(st, z, tv, rc, t, t == t_begin, a.seed);
+      epilogue<MODE>(st, z, tv, rc, t, t == t_begin, a.seed, kz * tmax[t]);
     }
   }
   finish<MODE>(st, rc, row, split, a, h == 0);
@@ -563,7 +612,10 @@ hipError_t launch_bias_pass(int mode, bool bf16, const BiasPassArgs& a, hipStrea
   TimingScope timing(mode == kModeDraft ? "draft_bias" : (mode == kModeCstar ? "cstar_bias" : "residual_bias"), stream);
   const dim3 grid(a.nsplit, (a.nrows + kRowsPerBlock - 1) / kRowsPerBlock);
   const dim3 block(kThreads);
-  if (bf16 && a.vec_ok) {
+  if (bf16 && mode == kModeDraft && a.zout) {
+    if (a.vec_ok) hipLaunchKernelGGL((k_bias_bf16<kModeDraft, 2, true, true>), grid, block, 0, stream, a);
+    else hipLaunchKernelGGL((k_bias_bf16<kModeDraft, 2, false, true>), grid, block, 0, stream, a);
+  } else if (bf16 && a.vec_ok) {
     if (mode == kModeDraft) hipLaunchKernelGGL((k_bias_bf16<kModeDraft, 2, true>), grid, block, 0, stream, a);
     else if (mode == kModeCstar) hipLaunchKernelGGL((k_bias_bf16<kModeCstar, 2, true>), grid, block, 0, stream, a);
     else hipLaunchKernelGGL((k_bias_bf16<kModeResidual, 2, true>), grid, block, 0, stream, a);

@@ -24,10 +24,16 @@ constexpr float kLn2 = 0.6931471805599453f;
 constexpr uint32_t kStreamDraft = 0, kStreamAccept = 1, kStreamResidual = 2, kStreamBonus = 3;
 constexpr uint32_t kMemberStream = 4;
 
-// Error bounds of the binary32 block scores of the split passes (see
-// BlockCands): |score32 - score64| <= kScoreAbs + kScoreRel * |max logit of
-// the block|, which covers the rounding of the logits, of the 32-term sums,
-// of the hardware exp2/log2 and of the Gumbel transform with a wide margin.
+// Error bound of a binary32 block score (log-mass + Gumbel variate, see
+// BlockCands) against its exact value:
+//   |score32 - score| <= kScoreAbs + kScoreRel |m| + dz,
+// m the block's largest logit.  dz = kContractErr ||W1[x]||_1 max|W2| over
+// the tile bounds the contraction error of every logit (zero where no bias is
+// added); a log-sum-exp moves by at most its inputs' largest error.  The other
+// two terms cover the rest, with wide margins: the rounding of z = U + B
+// (2^-24 |z|, whose weighted mean over the block is at most |m| + 12), the
+// exp2 arguments and results, the 32-term sum, the log2 and the binary32
+// Gumbel transform (each a few 2^-24 relative, at most ~2^-20 absolute).
 constexpr float kScoreAbs = 0x1p-12f;
 constexpr float kScoreRel = 0x1p-17f;
 

@@ -1,9 +1,8 @@
-// draft_epilogue.h -- the draft's per-tile epilogue, shared by the split bias
-// pass and the persistent draft kernel: for one row and one 32-token block
-// (lane pair n, n + 32, 16 logits each) the running log-sum-exp of
-// z = U_k + B_k and the block's score log-mass + Gumbel variate, bracketed by
-// its binary32 error bound, for the first level of the two-level Gumbel-max
-// draw from p_k = softmax(z) (summary page §3.1).
+// draft_epilogue.h -- the draft's per-tile epilogue: for one row and one
+// 32-token block (lane pair n, n + 32, 16 logits each) the running
+// log-sum-exp of z = U_k + B_k and the block's score log-mass + Gumbel
+// variate, bracketed by its binary32 error bound, for the first level of the
+// two-level Gumbel-max draw from p_k = softmax(z) (summary page §3.1).
 #pragma once
 
 #include "device_common.h"
@@ -51,9 +50,11 @@ struct DraftLane {
 // z[j] = logit of token 32 t + 16 h + j of row (r, k) (-inf at or beyond V);
 // `first` marks the first block of the lane's range (the Philox block of
 // four block words is fetched there and at every fourth block).  Exponentials
-// are taken in base 2 with the scaling folded into one fma.
+// are taken in base 2 with the scaling folded into one fma.  dz bounds the
+// error of every logit of the block; the block's log-mass moves by at most
+// that much (a log of a weighted mean of exp(error)), so it widens the bracket.
 __device__ __forceinline__ void draft_block_epilogue(DraftLane& st, const float* z, int r, int k,
-                                                     int t, bool first, uint64_t seed) {
+                                                     int t, bool first, uint64_t seed, float dz) {
   if (first || (t & 3) == 0) st.words = noise_block(seed, kStreamDraft, r, k, (uint32_t)t >> 2);
   const float mt = max_halves(max16(z));
   if (mt == -INFINITY) return;  // block without mass
@@ -69,7 +70,7 @@ __device__ __forceinline__ void draft_block_epilogue(DraftLane& st, const float*
     st.S += (double)(s * __builtin_amdgcn_exp2f((mt - st.M) * kLog2e));
   }
   const float sc = fmaf(__builtin_amdgcn_logf(s), kLn2, mt) + gumbel_f32(word_of(st.words, t & 3));
-  const float d = fmaf(kScoreRel, fabsf(mt), kScoreAbs);
+  const float d = fmaf(kScoreRel, fabsf(mt), kScoreAbs) + dz;
   st.cand.add(sc - d, sc + d, t);
 }
 

@@ -13,6 +13,27 @@ constexpr int kSteps = kRank / 16;
 
 enum BiasMode { kModeDraft = 0, kModeCstar = 1, kModeResidual = 2 };
 
+// Bytes of the packed W2 tiles (bf16: 16 KB MFMA tiles of 32 tokens; binary32:
+// the transposed matrix padded to whole tiles).  The per-tile max|W2| array
+// (one float per tile) follows them in the same buffer.
+__host__ __device__ inline int64_t w2_tiles_bytes(bool bf16, int ntiles) {
+  return bf16 ? (int64_t)ntiles * kSteps * 64 * 16 : (int64_t)ntiles * kTile * kRank * 4;
+}
+__host__ __device__ inline float* w2_tile_absmax(void* W2p, bool bf16, int ntiles) {
+  return reinterpret_cast<float*>(static_cast<char*>(W2p) + w2_tiles_bytes(bf16, ntiles));
+}
+__host__ __device__ inline const float* w2_tile_absmax(const void* W2p, bool bf16, int ntiles) {
+  return reinterpret_cast<const float*>(static_cast<const char*>(W2p) + w2_tiles_bytes(bf16, ntiles));
+}
+
+// Error bound of the binary32 contraction.  The split passes form
+// B_v = sum_i W1[x, i] W2[i, v] with binary32 products and sums starting from
+// zero (256 roundings at most), then z_v = U_v + B_v with one more rounding:
+// |z_v - exact| <= 256 u S_v + u |z_v|, u = 2^-24, S_v = sum_i |W1[x,i] W2[i,v]|
+// <= ||W1[x]||_1 max_{i, v in tile} |W2[i,v]|.  kContractErr = 2^-15 covers
+// 256 u twice over (the rounding of the L1 norm itself included).
+constexpr float kContractErr = 0x1p-15f;
+
 // Brackets one kernel launch with HIP events when library timing is enabled
 // (dspark_timing_enable); a no-op otherwise.
 class TimingScope {
@@ -76,6 +97,7 @@ struct BiasPassArgs {
   BlockCands cand;            // draft: blocks of p^d; residual: blocks of max(0, p^t - p^d)
   BlockCands cand_f;          // residual: blocks of p^t (empty-residual fallback)
   float* wpos;                // residual: residual mass seen by the split
+  float* zout;                // draft, optional: every logit z = U + B [R, gamma, V]
 };
 
 struct BiasGeometry {
@@ -199,6 +221,7 @@ hipError_t launch_finalize(int R, int gamma, const VerifyWs& w, float* cstar, hi
 
 // ---- other stages ---------------------------------------------------------
 hipError_t launch_pack_w2(bool bf16, int V, const void* W2, void* W2p, hipStream_t stream);
+hipError_t launch_logpd(int rows, int V, const double* lse, float* zl, hipStream_t stream);
 hipError_t launch_confidence(bool w1_bf16, int R, int gamma, int V, int H, const uint16_t* h,
                              const float* w, const float* temps, const void* W1,
                              const int32_t* anchors, const int32_t* tokens, float* c,

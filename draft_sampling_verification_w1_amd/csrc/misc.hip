@@ -30,6 +30,26 @@ __global__ __launch_bounds__(256) void k_pack_w2_bf16(int V, int ntiles, const u
   out[g] = (u32x4){w[0], w[1], w[2], w[3]};
 }
 
+// Largest |W2[i][v]| over the rank and the 32 tokens of each tile (tokens
+// below V), one workgroup per tile: the per-tile factor of the contraction's
+// error bound that the split passes use to bracket their binary32 scores.
+template <typename E>
+__global__ __launch_bounds__(kRank) void k_tile_absmax(int V, const E* W2, float* tmax) {
+  __shared__ float part[kRank / 64];
+  const int t = blockIdx.x;
+  const int i = threadIdx.x;  // rank index
+  float m = 0.f;
+  for (int j = 0; j < kTile; ++j) {
+    const int v = t * kTile + j;
+    if (v < V) m = fmaxf(m, fabsf(elem_at(W2, (int64_t)i * V + v)));
+  }
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
+  if ((i & 63) == 0) part[i >> 6] = m;
+  __syncthreads();
+  if (i == 0) tmax[t] = fmaxf(fmaxf(part[0], part[1]), fmaxf(part[2], part[3]));
+}
+
 // Transposed f32 W2: out[v][i] = W2[i][v], zero rows for v >= V.
 __global__ __launch_bounds__(256) void k_pack_w2_f32(int V, int vpad, const float* W2, float* out) {
   const int64_t g = (int64_t)blockIdx.x * 256 + threadIdx.x;
@@ -80,19 +100,41 @@ __global__ __launch_bounds__(256) void k_confidence(int R, int gamma, int V, int
   if (lane == 0) c[row] = (float)(1.0 / (1.0 + exp(-s / (double)temps[k - 1])));
 }
 
+// log p^d = z - lse per drafted row, in place over the logits the draft
+// stored: the difference in binary64, rounded once to binary32.
+__global__ __launch_bounds__(256) void k_logpd(int V, const double* lse, float* zl) {
+  const int64_t row = blockIdx.y;
+  const double l = lse[row];
+  float* p = zl + row * (int64_t)V;
+  for (int v = blockIdx.x * 256 + threadIdx.x; v < V; v += gridDim.x * 256)
+    p[v] = (float)((double)p[v] - l);
+}
+
 }  // namespace
+
+hipError_t launch_logpd(int rows, int V, const double* lse, float* zl, hipStream_t stream) {
+  TimingScope timing("logpd", stream);
+  const int chunks = (V + 4095) / 4096;
+  hipLaunchKernelGGL(k_logpd, dim3(chunks, rows), dim3(256), 0, stream, V, lse, zl);
+  return hipGetLastError();
+}
 
 hipError_t launch_pack_w2(bool bf16, int V, const void* W2, void* W2p, hipStream_t stream) {
   TimingScope timing("pack_w2", stream);
   const int ntiles = (V + kTile - 1) / kTile;
+  float* tmax = w2_tile_absmax(W2p, bf16, ntiles);
   if (bf16) {
     const int64_t n = (int64_t)ntiles * kSteps * 64;
     hipLaunchKernelGGL(k_pack_w2_bf16, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, V,
                        ntiles, (const uint16_t*)W2, (u32x4*)W2p);
+    hipLaunchKernelGGL(k_tile_absmax<uint16_t>, dim3(ntiles), dim3(kRank), 0, stream, V,
+                       (const uint16_t*)W2, tmax);
   } else {
     const int64_t n = (int64_t)ntiles * kTile * kRank;
     hipLaunchKernelGGL(k_pack_w2_f32, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, V,
                        ntiles * kTile, (const float*)W2, (float*)W2p);
+    hipLaunchKernelGGL(k_tile_absmax<float>, dim3(ntiles), dim3(kRank), 0, stream, V,
+                       (const float*)W2, tmax);
   }
   return hipGetLastError();
 }

@@ -55,7 +55,8 @@ def lib() -> ctypes.CDLL:
         L.dspark_pack_w2.argtypes = [P, _vp, _vp, _vp]
         L.dspark_workspace_bytes.argtypes = [P]
         L.dspark_workspace_bytes.restype = ctypes.c_size_t
-        L.dspark_draft_step.argtypes = [P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
+        L.dspark_draft_step.argtypes = [P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                        ctypes.c_size_t, _vp]
         L.dspark_verify.argtypes = [P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                     _vp, _vp, _vp, ctypes.c_size_t, _vp]
         L.dspark_confidence.argtypes = [P, ctypes.c_int32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]
@@ -141,8 +142,10 @@ def pack_w2(W2: torch.Tensor, V: int) -> torch.Tensor:
     return out
 
 
-def draft_step(U, W1, W2p, anchors, seed: int, ws=None, out=None):
-    """Stage 1 (dspark_draft_step).  U [R, gamma, V]; returns (tokens, lse, logq)."""
+def draft_step(U, W1, W2p, anchors, seed: int, ws=None, out=None, logpd=None):
+    """Stage 1 (dspark_draft_step).  U [R, gamma, V]; returns (tokens, lse, logq).
+    ``logpd``: optional float32 [R, gamma, V] tensor that receives log p^d of
+    every drafted position (a parity/debug output; it costs a full write)."""
     R, gamma, V = U.shape
     _need(U, "U")
     _need(W1, "W1", dtype=U.dtype, shape=(V, 256))
@@ -158,9 +161,11 @@ def draft_step(U, W1, W2p, anchors, seed: int, ws=None, out=None):
                torch.empty((R, gamma), dtype=torch.float64, device=U.device),
                torch.empty((R, gamma), dtype=torch.float64, device=U.device))
     tokens, lse, logq = out
+    if logpd is not None:
+        _need(logpd, "logpd", dtype=torch.float32, shape=(R, gamma, V))
     _check(lib().dspark_draft_step(ctypes.byref(p), _ptr(U), _ptr(W1), _ptr(W2p), _ptr(anchors),
-                                   _ptr(tokens), _ptr(lse), _ptr(logq), _ptr(ws), ws.numel(),
-                                   _stream()))
+                                   _ptr(tokens), _ptr(lse), _ptr(logq), _ptr(logpd), _ptr(ws),
+                                   ws.numel(), _stream()))
     return tokens, lse, logq
 
 

@@ -26,10 +26,25 @@
  *     W1).
  *   - dtype: DSPARK_F32 (binary32) or DSPARK_BF16 (bfloat16 bit patterns) for
  *     U, T, W1 and W2.  The Markov-head rank must be 256 (the pages' default).
- *   - Random numbers: Philox4x32-10 (Salmon et al., SC'11) keyed by `seed`,
- *     counter (v>>2, k, r, stream), word v&3; uniform ((w>>9)+1/2) 2^-23;
- *     Gumbel -ln(-ln u).  Streams: 0 draft, 1 accept, 2 residual, 3 bonus.
- *     k is the 1-based block position, r the request index, v the token id.
+ *   - Random numbers: Philox4x32-10 (Salmon et al., SC'11) with key words
+ *     (seed mod 2^32, seed >> 32) and counter (i>>2, k, r, stream), taking word
+ *     i&3 of the output; r is the request index, k the 1-based block position
+ *     and i the element index within the stream (a token id or a block index,
+ *     below).  Uniform u = ((w>>9) + 1/2) 2^-23; Gumbel variate
+ *     G(stream, r, k, i) = -ln(-ln u).
+ *   - Categorical draws: every token the library samples is a two-level
+ *     Gumbel-max draw from softmax(w) over a row of V log-weights w (entries may
+ *     be -inf).  The vocabulary is cut into blocks b of 32 tokens
+ *     [32b, 32b+32), the last one shorter when 32 does not divide V, and
+ *       block  b* = argmax_b ( log sum_{v in b} exp(w_v) + G(S, r, k, b) ),
+ *       token  x  = argmax_{v in b*} ( w_v + G(S + 4, r, k, v) ),
+ *     the lowest block, then the lowest token, winning exact ties (a block with
+ *     no finite entry never wins).  P(x = v) = softmax(w)_v exactly.  The
+ *     streams S (block) / S + 4 (member) are 0 / 4 for the draft, 2 / 6 for the
+ *     residual draw and 3 / 7 for the bonus draw; stream 1 holds the acceptance
+ *     uniforms (element i = 0).  The library takes each decision in binary64 on
+ *     the stored inputs; its binary32 screening only skips blocks that a
+ *     proven error bound shows cannot win.
  *   - No C++ exception crosses this interface.
  */
 #ifndef DSPARK_H_
@@ -72,11 +87,14 @@ size_t dspark_w2_packed_bytes(const dspark_problem* p);
 
 /* Repack the Markov-head factor W2 [rank, V] into the vocabulary-major layout
  * the kernels stream (a once-per-model weight preparation, not part of a round).
- * W2p must hold dspark_w2_packed_bytes(p) bytes, 256-byte aligned.
- *   bf16: 32-token tiles; tile t holds 16 steps x 64 lanes x 8 values, entry
+ * W2p must hold dspark_w2_packed_bytes(p) bytes, 256-byte aligned.  With
+ * n = ceil(V/32) tiles of 32 tokens:
+ *   bf16: tile t holds 16 steps x 64 lanes x 8 values, entry
  *         ((t*16 + s)*64 + l)*8 + e = W2[128*(l/32) + 8*s + e][32*t + pi(l%32)],
- *         pi(m) = 16*((m>>2)&1) + 4*(m>>3) + (m&3), zero beyond V.
- *   f32:  W2 transposed, [ceil(V/32)*32, rank], zero rows beyond V. */
+ *         pi(m) = 16*((m>>2)&1) + 4*(m>>3) + (m&3), zero beyond V (n*16 KB).
+ *   f32:  W2 transposed, [n*32, rank], zero rows beyond V.
+ * Then n floats: tile t's max |W2[i][v]| over i < rank and its tokens v < V
+ * (the factor of the contraction's error bound). */
 int dspark_pack_w2(const dspark_problem* p, const void* W2, void* W2p, void* stream);
 
 /* Workspace bytes needed by dspark_draft_step and dspark_verify for problem p
@@ -87,14 +105,17 @@ size_t dspark_workspace_bytes(const dspark_problem* p);
  * For k = 1..gamma and every request r, with x_0 = anchors[r]:
  *   z_v = U[r,k-1,v] + sum_i W1[x_{k-1}, i] W2[i, v]      (rank-256 bias B_k)
  *   lse[r,k-1]  = log sum_v exp(z_v)                     (p^d_k = softmax(z))
- *   x_k         = argmax_v (z_v + Gumbel(stream 0, r, k, v)), lowest v on ties
+ *   x_k         = the two-level draw from softmax(z) with streams 0 / 4 at (r, k)
  *   logq[r,k-1] = z_{x_k} - lse[r,k-1]                   (log p^d_k(x_k))
  * U: [R, gamma, V] dtype; W1: [V, 256] dtype; W2p: packed W2; anchors: [R] int32.
  * Outputs: tokens [R, gamma] int32, lse and logq [R, gamma] float64.
+ * logpd: NULL, or float32 [R, gamma, V] that receives log p^d_k(v) = z_v - lse
+ * of every position (a parity / debugging output that costs a full write;
+ * z in binary32, the difference in binary64 rounded to binary32).
  * ws: dspark_workspace_bytes(p) bytes, 256-byte aligned. */
 int dspark_draft_step(const dspark_problem* p, const void* U, const void* W1, const void* W2p,
                       const int32_t* anchors, int32_t* tokens, double* lse, double* logq,
-                      void* ws, size_t ws_bytes, void* stream);
+                      float* logpd, void* ws, size_t ws_bytes, void* stream);
 
 /* Stage 2 -- standard speculative rejection sampling with bonus token, and the
  * analytic acceptance c*.  [P1 요약, §3.2.1; P2 배경]
@@ -105,9 +126,11 @@ int dspark_draft_step(const dspark_problem* p, const void* U, const void* W1, co
  *   cstar[r,k-1] = sum_v min(p^d_k, p^t_k) = 1 - ||p^d_k - p^t_k||_1 / 2
  *   accept x_k iff ln u < ln p^t_k(x_k) - logq[r,k-1], u = uniform(stream 1, r, k, v=0)
  * n_accept[r] = number of leading accepted positions.  If a position k* <= l_r
- * is rejected, out_token[r] = argmax_v (ln max(0, p^t - p^d)_v + Gumbel(2, r, k*, v))
- * (falling back to ln p^t if that residual is empty); otherwise out_token[r] =
- * argmax_v (T[r,l_r,v] + Gumbel(3, r, l_r+1, v)) -- the bonus draw from p^t_{l_r+1}.
+ * is rejected, out_token[r] = the two-level draw from the normalised
+ * max(0, p^t_{k*} - p^d_{k*}) (log-weights ln max(0, p^t - p^d)) with streams
+ * 2 / 6 at (r, k*), or from p^t_{k*} with the same streams if no entry has
+ * p^t > p^d in binary64; otherwise out_token[r] = the two-level draw from
+ * softmax(T[r,l_r]) = p^t_{l_r+1} with streams 3 / 7 at (r, l_r + 1) (bonus).
  * T: [R, gamma+1, V] dtype (row gamma is the bonus row).  tokens, lse_d, logq:
  * stage-1 outputs.  lengths: [R] int32 in [0, gamma] or NULL.
  * Outputs: cstar [R, gamma] float32 (NaN for k > l_r); n_accept, out_token [R]

@@ -31,11 +31,16 @@
  * P(block) P(v | block) = softmax(w)_v.
  */
 #include <math.h>
+#include <omp.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
 
 #define ORACLE_API __attribute__((visibility("default")))
+
+/* Thread count of the row loops below (OpenMP; timing of the CPU baseline). */
+ORACLE_API void oracle_set_threads(int n) { omp_set_num_threads(n > 0 ? n : 1); }
+ORACLE_API int oracle_max_threads(void) { return omp_get_max_threads(); }
 
 /* Entries per sampling block of the two-level Gumbel-max draw (READING). */
 #define ORACLE_SAMPLE_BLOCK 32

@@ -112,8 +112,19 @@ def lib() -> ctypes.CDLL:
                                      _f64p, ctypes.c_int64, _f32p, _i64p, _i64p, _f32p]
         L.oracle_threshold_sweep.argtypes = [ctypes.c_int64, ctypes.c_int64, _f32p, _i32p,
                                              ctypes.c_int64, _f64p, _i64p, _i64p]
+        L.oracle_set_threads.argtypes = [ctypes.c_int]
+        L.oracle_max_threads.restype = ctypes.c_int
         _lib = L
     return _lib
+
+
+def set_threads(n: int):
+    """Threads of the oracle's OpenMP row loops."""
+    lib().oracle_set_threads(int(n))
+
+
+def max_threads() -> int:
+    return int(lib().oracle_max_threads())
 
 
 def _p(a: np.ndarray, ptype):

@@ -18,6 +18,18 @@ from oracle import oracle as O
 
 RTOL, ATOL, TIE = 1e-4, 1e-6, 1e-6
 
+# Running totals over every GPU comparison of the session: draws compared
+# (draft tokens, acceptance decisions, final draws), near-ties among them, and
+# the largest deviations of the normalisers and of the acceptance log-ratio
+# from the oracle's.  The last GPU test of the session checks the tie budget.
+STATS = {"draws": 0, "ties": 0, "max_lse_d_err": 0.0, "max_lse_t_err": 0.0,
+         "max_rho_err": 0.0, "max_logpd_err": 0.0, "logpd_values": 0}
+
+
+def _track(key, value):
+    if np.isfinite(value) and value > STATS[key]:
+        STATS[key] = float(value)
+
 
 def log(msg: str):
     print(msg, flush=True)
@@ -73,6 +85,7 @@ def compare_draft(od, tokens, lse, logq, requests=None):
                 log(f"near-tie draft r={r} k={k+1} margin={m:.2e}")
                 break
             compared += 1
+            _track("max_lse_d_err", abs(lse[r, k] - od["lse"][i, k]))
             np.testing.assert_allclose(lse[r, k], od["lse"][i, k], rtol=RTOL, atol=ATOL,
                                        err_msg=f"lse r={r} k={k+1}")
             # logq = ln p^d(x): p^d within RTOL relative is logq within RTOL absolute
@@ -80,16 +93,30 @@ def compare_draft(od, tokens, lse, logq, requests=None):
                                        err_msg=f"logq r={r} k={k+1}")
             np.testing.assert_allclose(np.exp(logq[r, k]), np.exp(od["logq"][i, k]), rtol=RTOL,
                                        atol=ATOL, err_msg=f"p^d(x) r={r} k={k+1}")
+    STATS["draws"] += compared + ties
+    STATS["ties"] += ties
     return compared, ties
 
 
-def compare_verify(ov, g, requests=None):
+def compare_verify(ov, g, requests=None, rho=None):
     """Compare GPU verify outputs (numpy dict) with the oracle's ``ov`` for its
-    requests.  Returns (n_requests_compared, n_ties)."""
+    requests.  ``rho`` = (T, tokens, logq_in, logq_oracle) also tracks how far
+    the GPU's acceptance log-ratio (T[x] - lse_t) - logq_in is from the
+    oracle's (T[x] - lse_t) - logq_oracle (T stored target logits [R, gamma+1,
+    V], tokens and logq_in [R, gamma] by request id, logq_oracle [n, gamma] in
+    ``ov``'s row order).  Returns (n_requests_compared, n_ties)."""
     req = ov["requests"] if requests is None else requests
-    ties = 0
+    ties = decisions = 0
     gamma = ov["cstar"].shape[1]
     for i, r in enumerate(req):
+        if rho is not None and g.get("lse_t") is not None:
+            T, tokens, logq_in, logq_or = rho
+            for k in range(int(np.sum(ov["accept_mask"][i] != 255))):
+                x = int(tokens[r, k])
+                tx = float(O.to_f64(T[r, k, x:x + 1])[0])
+                rho_g = (tx - g["lse_t"][r, k]) - logq_in[r, k]
+                rho_o = (tx - ov["lse_t"][i, k]) - logq_or[i, k]
+                _track("max_rho_err", abs(rho_g - rho_o))
         oc, gc = ov["cstar"][i], g["cstar"][r]
         assert np.array_equal(np.isnan(oc), np.isnan(gc)), f"c* NaN pattern r={r}"
         fin = ~np.isnan(oc)
@@ -97,6 +124,8 @@ def compare_verify(ov, g, requests=None):
         if g.get("lse_t") is not None:
             olt, glt = ov["lse_t"][i], g["lse_t"][r]
             fin = ~np.isnan(olt)
+            if fin.any():
+                _track("max_lse_t_err", np.max(np.abs(glt[fin] - olt[fin])))
             np.testing.assert_allclose(glt[fin], olt[fin], rtol=RTOL, atol=ATOL, err_msg=f"lse_t r={r}")
         tie_here = False
         for k in range(gamma):
@@ -108,6 +137,9 @@ def compare_verify(ov, g, requests=None):
                 tie_here = True
                 ties += 1
                 break
+            if om == 255:
+                break
+            decisions += 1
             if om != 1:
                 break
         if tie_here:
@@ -119,7 +151,38 @@ def compare_verify(ov, g, requests=None):
                              f"{ov['out_token'][i]} margin {m:.3e}")
             log(f"near-tie final draw r={r} margin={m:.2e}")
             ties += 1
+        else:
+            decisions += 1
+    STATS["draws"] += decisions + ties
+    STATS["ties"] += ties
     return len(req), ties
+
+
+def compare_logpd(logpd_g, U, W1, W2f, anchors, tok_g, od, requests=None, k_range=None):
+    """Element-by-element check of the draft's log p^d output [R, gamma, V]
+    against the oracle: p^d within RTOL relative / ATOL absolute, for every
+    (request, position) whose earlier drafted tokens equal the oracle's (the
+    rows are conditioned on them).  ``od`` is the oracle draft of ``requests``
+    (rows in that order).  Returns the number of rows compared."""
+    req = od["requests"] if requests is None else requests
+    gamma = od["tokens"].shape[1]
+    rows = 0
+    for k in (range(1, gamma + 1) if k_range is None else k_range):
+        same = np.array([np.array_equal(tok_g[r, :k - 1], od["tokens"][i, :k - 1])
+                         for i, r in enumerate(req)])
+        sel = np.asarray(req)[same]
+        if sel.size == 0:
+            continue
+        prev = anchors[sel] if k == 1 else od["tokens"][same, k - 2]
+        z = O.draft_logits(U[sel, k - 1, :], W1, W2f, prev)
+        lpd_o = z - od["lse"][same, k - 1][:, None]
+        lpd_g = logpd_g[sel, k - 1, :].astype(np.float64)
+        _track("max_logpd_err", np.max(np.abs(lpd_g - lpd_o)))
+        np.testing.assert_allclose(np.exp(lpd_g), np.exp(lpd_o), rtol=RTOL, atol=ATOL,
+                                   err_msg=f"p^d at position {k}")
+        STATS["logpd_values"] += lpd_g.size
+        rows += sel.size
+    return rows
 
 
 def compare_schedule(os_, a_g, g):

@@ -49,7 +49,8 @@ def test_problem_validation(L, kw, code):
     p = _p(L, **kw)
     assert lib.dspark_workspace_bytes(ctypes.byref(p)) == 0
     assert lib.dspark_w2_packed_bytes(ctypes.byref(p)) == 0
-    st = lib.dspark_draft_step(ctypes.byref(p), None, None, None, None, None, None, None, None, 0, None)
+    st = lib.dspark_draft_step(ctypes.byref(p), None, None, None, None, None, None, None, None, None,
+                               0, None)
     assert st == code
     assert lib.dspark_last_error()
 
@@ -57,18 +58,19 @@ def test_problem_validation(L, kw, code):
 def test_sizes(L):
     lib = L.lib()
     p = _p(L, dtype=1, V=151936, R=256, gamma=16)
-    assert lib.dspark_w2_packed_bytes(ctypes.byref(p)) == 151936 * 256 * 2
+    # packed tiles, then one float per 32-token tile (its max |W2|)
+    assert lib.dspark_w2_packed_bytes(ctypes.byref(p)) == 151936 * 256 * 2 + 4748 * 4
     assert lib.dspark_workspace_bytes(ctypes.byref(p)) > 0
     p = _p(L, dtype=0, V=4097)
-    assert lib.dspark_w2_packed_bytes(ctypes.byref(p)) == 4128 * 256 * 4  # padded to 32-token tiles
+    assert lib.dspark_w2_packed_bytes(ctypes.byref(p)) == 4128 * 256 * 4 + 129 * 4  # whole tiles
 
 
 def test_null_tensors_rejected(L):
     lib = L.lib()
     p = _p(L)
     fake = ctypes.c_void_p(0x1000)
-    assert lib.dspark_draft_step(ctypes.byref(p), fake, fake, None, fake, fake, fake, fake, fake,
-                                 1 << 30, None) == -1
+    assert lib.dspark_draft_step(ctypes.byref(p), fake, fake, None, fake, fake, fake, fake, None,
+                                 fake, 1 << 30, None) == -1
     assert lib.dspark_verify(ctypes.byref(p), fake, fake, fake, fake, fake, fake, fake, None, None,
                              fake, fake, fake, None, None, fake, 1 << 30, None) == -1
     assert lib.dspark_pack_w2(ctypes.byref(p), None, fake, None) == -1
@@ -82,11 +84,11 @@ def test_workspace_checks(L):
     need = lib.dspark_workspace_bytes(ctypes.byref(p))
     fake = ctypes.c_void_p(0x10000)
     # missing, too small, misaligned -- all rejected before any launch
-    assert lib.dspark_draft_step(ctypes.byref(p), fake, fake, fake, fake, fake, fake, fake, None, need,
-                                 None) == -4
-    assert lib.dspark_draft_step(ctypes.byref(p), fake, fake, fake, fake, fake, fake, fake, fake,
-                                 need - 1, None) == -4
-    assert lib.dspark_draft_step(ctypes.byref(p), fake, fake, fake, fake, fake, fake, fake,
+    assert lib.dspark_draft_step(ctypes.byref(p), fake, fake, fake, fake, fake, fake, fake, None,
+                                 None, need, None) == -4
+    assert lib.dspark_draft_step(ctypes.byref(p), fake, fake, fake, fake, fake, fake, fake, None,
+                                 fake, need - 1, None) == -4
+    assert lib.dspark_draft_step(ctypes.byref(p), fake, fake, fake, fake, fake, fake, fake, None,
                                  ctypes.c_void_p(0x10010), need, None) == -4
     assert b"workspace" in lib.dspark_last_error()
 

@@ -24,7 +24,7 @@ def test_write_traffic_scales_by_the_copy(tmp_path, monkeypatch):
     # three 1 MiB copies (3 MiB read and written): the fetch counter reads half,
     # the write counter reads all of it, so the scales are 2 and 1
     copy = [("__amd_rocclr_copyBuffer", 512.0)] * 3
-    draft = "void dspark::(anonymous namespace)::k_bias_bf16<0, 2, true>(dspark::BiasPassArgs)"
+    draft = "void dspark::(anonymous namespace)::k_bias_bf16<0, 2, true, false>(dspark::BiasPassArgs)"
     _write(tmp_path / "f.csv", "FETCH_SIZE", copy + [(draft, 1000.0), (draft, 1200.0)])
     _write(tmp_path / "w.csv", "WRITE_SIZE", [("__amd_rocclr_copyBuffer", 1024.0)] * 3 +
            [(draft, 10.0), (draft, 30.0)])

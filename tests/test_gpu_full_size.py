@@ -1,18 +1,22 @@
 """GPU parity at the workloads' full sizes (C2 Qwen3-4B-shaped, C3 high
 concurrency, C4 large vocabulary, C5 full scheduled round), in the launch
 configuration the benchmark times: the whole batch goes through the C ABI and
-sampled requests are compared with the oracle one by one (a request's draft,
-verification and confidence depend on its own inputs only).  The scheduler,
-which couples requests, is compared on the whole batch with the oracle's
-Algorithm 1 run on the same survival inputs.
+every request is compared with the oracle (a request's draft, verification and
+confidence depend on its own inputs only; the scheduler, which couples
+requests, is compared on the whole batch).  At C2 and C3 the draft runs a
+second time with its log p^d output, which is compared with the oracle element
+by element.
 
-Target logits of the sampled requests are built from the oracle's draft
-logits; the other requests get a draft-independent stand-in (never compared).
+Target logits are built from the ORACLE's draft logits (draft logits + noise,
+the workloads' recipe), so no oracle input comes from the HIP path.  A request
+whose GPU draft parted from the oracle's at a logged near-tie is left out of
+the verify comparison (its targets follow the oracle's tokens).
 """
 import numpy as np
 import pytest
 
-from parity_util import compare_draft, compare_schedule, compare_verify, log, to_dev
+from parity_util import (compare_draft, compare_logpd, compare_schedule, compare_verify, log,
+                         to_dev)
 
 pytestmark = [pytest.mark.gpu, pytest.mark.slow]
 
@@ -27,32 +31,22 @@ def dev():
     return dspark
 
 
-def _sample(R, seed):
-    rng = np.random.default_rng(seed)
-    s = {0, R - 1, R // 3}
-    s.add(int(rng.integers(0, R)))
-    return np.array(sorted(s), np.int32)
-
-
-def _targets(cfg, inp, od_tokens_sample, sample, synth, O):
-    """T [R, gamma+1, V]: oracle draft logits + noise for the sampled requests,
-    backbone rows + noise for the others."""
-    T = np.empty((cfg.R, cfg.gamma + 1, cfg.V), np.uint16)
+def _targets(cfg, inp, od_tokens, synth, O):
+    """T [R, gamma+1, V] in storage type: the oracle's draft logits + noise
+    (one fp64 product per position over the whole batch)."""
+    R, g, V = cfg.R, cfg.gamma, cfg.V
     W2f = O.to_f64(inp["W2"])
-    pos = {int(r): i for i, r in enumerate(sample)}
-    for r in range(cfg.R):
-        if r in pos:
-            i = pos[r]
-            zd = O.draft_logits_all(inp["U"], inp["W1"], W2f, inp["anchors"][[r]],
-                                    od_tokens_sample[[i]], [r])[0]
-            base = zd.astype(np.float32)
-        else:
-            base = synth.bf16_bits_to_f32(inp["U"][r])
-        T[r] = synth.target_rows(cfg, r, base, inp["Ub"][r])
+    base = np.empty((R, g, V), np.float32)
+    for k in range(1, g + 1):
+        prev = inp["anchors"] if k == 1 else od_tokens[:, k - 2]
+        base[:, k - 1, :] = O.draft_logits(inp["U"][:, k - 1, :], inp["W1"], W2f, prev)
+    T = np.empty((R, g + 1, V), np.uint16)
+    for r in range(R):
+        T[r] = synth.target_rows(cfg, r, base[r], inp["Ub"][r])
     return T
 
 
-def _full_round(dev, name, with_confidence=False):
+def _full_round(dev, name, with_confidence=False, check_logpd=False):
     import time
     import torch
     from oracle import oracle as O
@@ -62,19 +56,30 @@ def _full_round(dev, name, with_confidence=False):
     W1, W2 = synth.weights(cfg)
     U, Ub = synth.backbone(cfg)
     inp = {"W1": W1, "W2": W2, "U": U, "Ub": Ub, "anchors": synth.anchors(cfg)}
-    sample = _sample(cfg.R, cfg.seed)
-    log(f"full size {name}: R={cfg.R} gamma={cfg.gamma} V={cfg.V}; inputs in {time.time() - t0:.1f}s; "
-        f"sampled requests {sample.tolist()}")
+    log(f"full size {name}: R={cfg.R} gamma={cfg.gamma} V={cfg.V}; inputs in {time.time() - t0:.1f}s")
 
     dU, dW1, dA = to_dev(U), to_dev(W1), to_dev(inp["anchors"])
     W2p = dev.pack_w2(to_dev(W2), cfg.V)
     tok, lse, logq = dev.draft_step(dU, dW1, W2p, dA, cfg.seed)
     torch.cuda.synchronize()
     tok_h, lse_h, logq_h = tok.cpu().numpy(), lse.cpu().numpy(), logq.cpu().numpy()
-    od = O.draft(U, W1, W2, inp["anchors"], cfg.seed, requests=sample)
-    n, ties = compare_draft(od, tok_h, lse_h, logq_h, requests=sample)
-    log(f"  draft: {n} sampled positions compared, {ties} near-ties")
+    t0 = time.time()
+    od = O.draft(U, W1, W2, inp["anchors"], cfg.seed)
+    n, ties = compare_draft(od, tok_h, lse_h, logq_h)
+    log(f"  draft: {n} positions compared (every request), {ties} near-ties; oracle "
+        f"{time.time() - t0:.1f}s")
     assert np.all((tok_h >= 0) & (tok_h < cfg.V))
+
+    if check_logpd:
+        lp = torch.empty((cfg.R, cfg.gamma, cfg.V), dtype=torch.float32, device="cuda")
+        tok2 = dev.draft_step(dU, dW1, W2p, dA, cfg.seed, logpd=lp)[0]
+        torch.cuda.synchronize()
+        assert torch.equal(tok2, tok), "the draft with the log p^d output drew other tokens"
+        t0 = time.time()
+        rows = compare_logpd(lp.cpu().numpy(), U, W1, O.to_f64(W2), inp["anchors"], tok_h, od)
+        del lp
+        log(f"  log p^d: {rows} rows x {cfg.V} compared element by element in "
+            f"{time.time() - t0:.1f}s")
 
     lengths = None
     if with_confidence:
@@ -98,16 +103,20 @@ def _full_round(dev, name, with_confidence=False):
             f"mean length {lengths.mean():.2f}")
 
     t0 = time.time()
-    T = _targets(cfg, inp, od["tokens"], sample, synth, O)
+    T = _targets(cfg, inp, od["tokens"], synth, O)
     log(f"  targets in {time.time() - t0:.1f}s")
     g = dev.verify(dU, dW1, W2p, dA, tok, lse, logq, to_dev(T),
                    None if lengths is None else to_dev(lengths), cfg.seed)
     torch.cuda.synchronize()
     gn = {k: (v.cpu().numpy() if v is not None else None) for k, v in g.items()}
-    ov = O.verify(U, W1, W2, inp["anchors"], tok_h, T, lengths, cfg.seed, requests=sample)
-    n, ties = compare_verify(ov, gn, requests=sample)
-    log(f"  verify: {n} sampled requests compared, {ties} near-ties; "
-        f"accepted {ov['n_accept'].tolist()}")
+    same = np.array([np.array_equal(tok_h[r], od["tokens"][r]) for r in range(cfg.R)])
+    req = np.nonzero(same)[0].astype(np.int32)
+    t0 = time.time()
+    ov = O.verify(U, W1, W2, inp["anchors"], tok_h, T, lengths, cfg.seed, requests=req, chunk=32)
+    n, ties = compare_verify(ov, gn, requests=req, rho=(T, tok_h, logq_h, od["logq"][req]))
+    log(f"  verify: {n} of {cfg.R} requests compared, {ties} near-ties; oracle "
+        f"{time.time() - t0:.1f}s; mean accepted {ov['n_accept'].mean():.3f}")
+    assert n >= cfg.R - 2
     # every request: lengths and token ranges are consistent
     L = np.full(cfg.R, cfg.gamma) if lengths is None else lengths
     assert np.all((gn["n_accept"] >= 0) & (gn["n_accept"] <= L))
@@ -130,11 +139,11 @@ def _full_round(dev, name, with_confidence=False):
 
 
 def test_full_size_qwen3_4b(dev):
-    _full_round(dev, "qwen3_4b")
+    _full_round(dev, "qwen3_4b", check_logpd=True)
 
 
 def test_full_size_high_concurrency(dev):
-    _full_round(dev, "high_concurrency")
+    _full_round(dev, "high_concurrency", check_logpd=True)
 
 
 def test_full_size_large_vocab(dev):

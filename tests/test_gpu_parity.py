@@ -5,8 +5,8 @@ oracle's upstream outputs."""
 import numpy as np
 import pytest
 
-from parity_util import (compare_draft, compare_schedule, compare_verify, build_target,
-                         gen_inputs, log, to_dev)
+from parity_util import (compare_draft, compare_logpd, compare_schedule, compare_verify,
+                         build_target, gen_inputs, log, to_dev)
 
 pytestmark = pytest.mark.gpu
 
@@ -21,20 +21,28 @@ def dev():
     return dspark
 
 
-def _run_case(dspark, cfg, lengths=None, check_schedule=True):
+def _run_case(dspark, cfg, lengths=None, check_schedule=True, inp=None):
+    """Draft (with its log p^d output, compared element by element), verify
+    and schedule of one workload against the oracle, stage by stage."""
     import torch
     from oracle import oracle as O
     from draft_sampling_verification_w1_amd import synth
     log(f"case {cfg.name} R={cfg.R} gamma={cfg.gamma} V={cfg.V} dtype={cfg.dtype}")
-    inp = gen_inputs(cfg)
+    inp = gen_inputs(cfg) if inp is None else inp
     od = O.draft(inp["U"], inp["W1"], inp["W2"], inp["anchors"], cfg.seed)
     U, W1, W2 = to_dev(inp["U"]), to_dev(inp["W1"]), to_dev(inp["W2"])
     anchors = to_dev(inp["anchors"])
     W2p = dspark.pack_w2(W2, cfg.V)
-    tok, lse, logq = dspark.draft_step(U, W1, W2p, anchors, cfg.seed)
+    lp = torch.empty((cfg.R, cfg.gamma, cfg.V), dtype=torch.float32, device="cuda")
+    tok, lse, logq = dspark.draft_step(U, W1, W2p, anchors, cfg.seed, logpd=lp)
     torch.cuda.synchronize()
-    n, ties = compare_draft(od, tok.cpu().numpy(), lse.cpu().numpy(), logq.cpu().numpy())
-    log(f"  draft: {n} positions compared, {ties} near-ties")
+    tok_h = tok.cpu().numpy()
+    n, ties = compare_draft(od, tok_h, lse.cpu().numpy(), logq.cpu().numpy())
+    rows = compare_logpd(lp.cpu().numpy(), inp["U"], inp["W1"], O.to_f64(inp["W2"]),
+                         inp["anchors"], tok_h, od)
+    log(f"  draft: {n} positions compared, {ties} near-ties; log p^d of {rows} rows")
+    tok0 = dspark.draft_step(U, W1, W2p, anchors, cfg.seed)[0]
+    assert torch.equal(tok0, tok), "the log p^d output changed the drafted tokens"
 
     T = build_target(cfg, inp, od["tokens"])
     ov = O.verify(inp["U"], inp["W1"], inp["W2"], inp["anchors"], od["tokens"], T, lengths, cfg.seed)
@@ -43,7 +51,7 @@ def _run_case(dspark, cfg, lengths=None, check_schedule=True):
                       cfg.seed)
     torch.cuda.synchronize()
     gn = {k: (v.cpu().numpy() if v is not None else None) for k, v in g.items()}
-    n, ties = compare_verify(ov, gn)
+    n, ties = compare_verify(ov, gn, rho=(T, od["tokens"], od["logq"], od["logq"]))
     fin = ov["cstar"][~np.isnan(ov["cstar"])]
     mean_c = f"{fin.mean():.4f}" if fin.size else "none verified"
     log(f"  verify: {n} requests compared, {ties} near-ties; mean c* {mean_c}, "
@@ -77,6 +85,69 @@ def test_bf16_shapes(dev, R, gamma, V):
     cfg = synth.scaled(synth.CONFIGS["qwen3_4b"], name=f"bf16_{R}x{gamma}x{V}", R=R, gamma=gamma,
                        V=V, n_sps=R * (gamma + 1))
     _run_case(dev, cfg)
+
+
+def test_large_weights_bracket(dev):
+    """W1, W2 ~ N(0, 1): the bias has magnitude ~16 while sum |W1 W2| ~ 160, so
+    the binary32 contraction error is large and cancelling.  The screening
+    bracket must follow it (its contraction term grows with ||W1||_1 max|W2|),
+    so that tokens still equal the binary64 draws."""
+    from draft_sampling_verification_w1_amd import synth
+    cfg = synth.scaled(synth.CONFIGS["qwen3_4b"], name="big_w", R=40, gamma=3, V=4099,
+                       w_sigma=1.0, n_sps=40 * 4)
+    _run_case(dev, cfg)
+
+
+def test_shift_head_bracket(dev):
+    """A 30 * I shift head: W1[x] = 30 e_(x mod 256) and W2[i, v] = 1 when
+    v = i + 1 (mod 256), so B(v | x) = 30 for every v = x + 1 (mod 256): a few
+    tokens per row carry +30 on top of U ~ N(0, 16), and the drafted chain
+    follows them.  Large, exact logits (|z| ~ 40) test the bracket's terms in
+    |max logit|."""
+    from draft_sampling_verification_w1_amd import synth
+    cfg = synth.scaled(synth.CONFIGS["qwen3_4b"], name="shift_head", R=24, gamma=4, V=3000,
+                       n_sps=24 * 5)
+    inp = gen_inputs(cfg)
+    V = cfg.V
+    W1 = np.zeros((V, 256), np.float32)
+    W1[np.arange(V), np.arange(V) % 256] = 30.0
+    W2 = np.zeros((256, V), np.float32)
+    v = np.arange(V)
+    W2[(v - 1) % 256, v] = 1.0
+    inp["W1"], inp["W2"] = synth.f32_to_bf16_bits(W1), synth.f32_to_bf16_bits(W2)
+    _run_case(dev, cfg, inp=inp)
+
+
+@pytest.mark.parametrize("shift", [1e-3, -1e-3])
+def test_empty_residual_fallback(dev, shift):
+    """Every first position is rejected (logq = +30 makes the acceptance
+    log-ratio below any ln u) and the target equals the draft exactly (W2 = 0,
+    T = U).  With lse_d lowered by 1e-3 every p^d = p e^(1e-3) exceeds p^t, the
+    residual max(0, p^t - p^d) is empty and the corrective token comes from
+    the fallback draw from p^t; with lse_d raised by 1e-3 the residual is p^t
+    times a constant, whose draw is the same token (a two-level draw is
+    unchanged by a constant shift of its log-weights).  Either way out_token
+    must equal the two-level draw from p^t_1 with streams 2 / 6 at (r, 1)."""
+    import torch
+    from oracle import oracle as O
+    from draft_sampling_verification_w1_amd import synth
+    cfg = synth.scaled(synth.CONFIGS["qwen3_4b"], name="empty_res", R=16, gamma=3, V=3000)
+    inp = gen_inputs(cfg)
+    W2 = np.zeros((256, cfg.V), np.uint16)
+    T = np.concatenate([inp["U"], inp["U"][:, :1]], axis=1)   # T[r, k] = U[r, k] exactly
+    od = O.draft(inp["U"], inp["W1"], W2, inp["anchors"], cfg.seed)
+    lse_in = od["lse"] + shift
+    logq_in = np.full_like(od["logq"], 30.0)
+    W2p = dev.pack_w2(to_dev(W2), cfg.V)
+    g = dev.verify(to_dev(inp["U"]), to_dev(inp["W1"]), W2p, to_dev(inp["anchors"]),
+                   to_dev(od["tokens"]), to_dev(lse_in), to_dev(logq_in), to_dev(T), None, cfg.seed)
+    torch.cuda.synchronize()
+    assert np.all(g["n_accept"].cpu().numpy() == 0)
+    got = g["out_token"].cpu().numpy()
+    for r in range(cfg.R):
+        row = O.to_f64(T[r, 0])
+        x, margin = O.two_level_draw(row - O.logsumexp(row), 32, cfg.seed, 2, 6, r, 1)
+        assert got[r] == x or margin < 1e-6, f"r={r}: gpu {got[r]} oracle {x} margin {margin:.2e}"
 
 
 def test_large_vocab_distributions_small(dev):
@@ -122,10 +193,16 @@ def test_pack_layout(dev):
     """Packed W2 follows the layout documented in include/dspark.h."""
     import torch
     V = 100
-    W2 = np.random.default_rng(0).integers(0, 65535, (256, V)).astype(np.uint16)
+    # arbitrary finite bf16 bit patterns (exponent below 0xFF: no inf or NaN)
+    W2 = (np.random.default_rng(0).integers(0, 65535, (256, V)) & 0xBFFF).astype(np.uint16)
     p = dev.pack_w2(to_dev(W2), V).cpu().numpy().view(np.uint16)
     ntiles = (V + 31) // 32
-    assert p.size == ntiles * 16 * 64 * 8
+    assert p.size == ntiles * 16 * 64 * 8 + ntiles * 2   # then one float per tile
+    tmax = p[ntiles * 16 * 64 * 8:].view(np.float32)
+    W2f = (W2.astype(np.uint32) << 16).view(np.float32)
+    for t in range(ntiles):
+        assert tmax[t] == np.abs(W2f[:, 32 * t:min(V, 32 * t + 32)]).max()
+    p = p[:ntiles * 16 * 64 * 8]
     pi = lambda m: 16 * ((m >> 2) & 1) + 4 * (m >> 3) + (m & 3)
     for t in range(ntiles):
         for s in range(16):
@@ -136,9 +213,12 @@ def test_pack_layout(dev):
                     ref = W2[k, v] if v < V else 0
                     assert p[((t * 16 + s) * 64 + l) * 8 + e] == ref
     Wf = np.random.default_rng(1).standard_normal((256, V)).astype(np.float32)
-    pf = dev.pack_w2(to_dev(Wf), V).cpu().numpy().view(np.float32).reshape(ntiles * 32, 256)
+    pf = dev.pack_w2(to_dev(Wf), V).cpu().numpy().view(np.float32)
+    tmax = pf[ntiles * 32 * 256:]
+    pf = pf[:ntiles * 32 * 256].reshape(ntiles * 32, 256)
     np.testing.assert_array_equal(pf[:V], Wf.T)
     assert np.all(pf[V:] == 0)
+    np.testing.assert_array_equal(tmax, [np.abs(Wf[:, 32 * t:32 * t + 32]).max() for t in range(ntiles)])
 
 
 @pytest.mark.parametrize("H,dtype", [(4096, "bf16"), (1003, "bf16"), (64, "f32")])
