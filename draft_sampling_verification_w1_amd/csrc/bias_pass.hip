@@ -174,12 +174,15 @@ struct LaneState<kModeResidual> {
 // taken in base 2 with the scaling folded into one fma.
 // dz bounds the binary32 contraction error of every logit of the tile
 // (kContractErr ||W1[x]||_1 max|W2| over the tile).
+// The draft passes the backbone logits u and the bias b separately (its
+// log-sums are rounded relative to the block maximum only, see
+// draft_block_epilogue); z = u + b for the other modes.
 template <int MODE>
 __device__ __forceinline__ void epilogue(LaneState<MODE>& st, const float* z, const float* tv,
                                          const RowCtx& rc, int t, bool first, uint64_t seed,
-                                         float dz) {
+                                         float dz, const float* u = nullptr) {
   if constexpr (MODE == kModeDraft) {
-    draft_block_epilogue(st, z, rc.r, rc.k, t, first, seed, dz);
+    draft_block_epilogue(st, u, z, rc.r, rc.k, t, first, seed, dz);
   } else if constexpr (MODE == kModeCstar) {
     float e[16];
 #pragma unroll
@@ -404,13 +407,23 @@ __device__ void bias_body(const BiasPassArgs& a, int split, int nsplit, int row_
         for (int tau = 0; tau < ST; ++tau) {
           const int t = c * ST + tau;
           if (t < t_end) {
-            // the chain accumulates B from zero (its error then scales with
-            // sum |W1 W2| only); the backbone logits are added after it
+            // draft and residual: the chain accumulates B from zero (its error
+            // then scales with sum |W1 W2| only, which the brackets use) and the
+            // backbone logits are added after it; c* (no bracket) seeds the
+            // accumulator with them, so that the chain yields z = U + B
             const int s0 = 4 * tau + 2 * h;
             const float dz = kz * tmax[t];
             f32x16 acc;
+            if constexpr (MODE == kModeCstar) {
+              float zu[16];
+              decode16(*reinterpret_cast<const u32x4*>(ru_lds + ((s0 ^ sw) * 16)),
+                       *reinterpret_cast<const u32x4*>(ru_lds + (((s0 + 1) ^ sw) * 16)), zu);
 #pragma unroll
-            for (int j = 0; j < 16; ++j) acc[j] = 0.f;
+              for (int j = 0; j < 16; ++j) acc[j] = zu[j];
+            } else {
+#pragma unroll
+              for (int j = 0; j < 16; ++j) acc[j] = 0.f;
+            }
             const u32x4* At = reinterpret_cast<const u32x4*>(ra_lds + tau * kTileBytesA) + lane;
             if constexpr (kBatchA) {
               // all 16 A fragments in flight before the chain starts (one LDS
@@ -427,23 +440,28 @@ __device__ void bias_body(const BiasPassArgs& a, int split, int nsplit, int row_
               for (int s = 0; s < kSteps; ++s)
                 acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(At[s * 64]), bop[s], acc, 0, 0, 0);
             }
-            float z[16];
-            decode16(*reinterpret_cast<const u32x4*>(ru_lds + ((s0 ^ sw) * 16)),
-                     *reinterpret_cast<const u32x4*>(ru_lds + (((s0 + 1) ^ sw) * 16)), z);
+            float z[16], zu[16];
+            if constexpr (MODE == kModeCstar) {
 #pragma unroll
-            for (int j = 0; j < 16; ++j) z[j] += acc[j];
+              for (int j = 0; j < 16; ++j) z[j] = acc[j];
+            } else {
+              decode16(*reinterpret_cast<const u32x4*>(ru_lds + ((s0 ^ sw) * 16)),
+                       *reinterpret_cast<const u32x4*>(ru_lds + (((s0 + 1) ^ sw) * 16)), zu);
+#pragma unroll
+              for (int j = 0; j < 16; ++j) z[j] = (MODE == kModeDraft) ? acc[j] : zu[j] + acc[j];
+            }
             if constexpr (ZOUT) {
               const int vb = t * kTile + 16 * h;
               if (zrow)
 #pragma unroll
                 for (int j = 0; j < 16; ++j)
-                  if (vb + j < a.V) zrow[vb + j] = z[j];
+                  if (vb + j < a.V) zrow[vb + j] = zu[j] + z[j];
             }
             float tv[16];
             if constexpr (kNeedT)
               decode16(*reinterpret_cast<const u32x4*>(rt_lds + ((s0 ^ sw) * 16)),
                        *reinterpret_cast<const u32x4*>(rt_lds + (((s0 + 1) ^ sw) * 16)), tv);
-            epilogue<MODE>(st, z, tv, rc, t, t == t_begin, a.seed, dz);
+            epilogue<MODE>(st, z, tv, rc, t, t == t_begin, a.seed, dz, zu);
           }
         }
       }
@@ -533,16 +551,17 @@ __global__ __launch_bounds__(kThreads) void k_bias_f32(const BiasPassArgs a) {
       for (int j = 0; j < 16; ++j) part[wave][j][lane] = acc[j];
       __syncthreads();
       if (wave == 0) {
-        float z[16], tv[16];
+        float z[16], zu[16], tv[16];
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
           float b = part[0][j][lane];
           for (int w = 1; w < kWaves; ++w) b += part[w][j][lane];
-          z[j] = (rc.active && vb + j < a.V) ? ur[vb + j] + b : -INFINITY;
+          zu[j] = (rc.active && vb + j < a.V) ? ur[vb + j] : -INFINITY;
+          z[j] = (MODE == kModeDraft) ? b : zu[j] + b;  // the draft takes u and b apart
           tv[j] = (kNeedT && rc.active && vb + j < a.V) ? tr[vb + j] : -INFINITY;
-          if (zrow && vb + j < a.V) zrow[vb + j] = z[j];
+          if (zrow && vb + j < a.V) zrow[vb + j] = zu[j] + b;
         }
-        epilogue<MODE>(st, z, tv, rc, t, t == t_begin, a.seed, kz * tmax[t]);
+        epilogue<MODE>(st, z, tv, rc, t, t == t_begin, a.seed, kz * tmax[t], zu);
       }
       __syncthreads();
     }
@@ -579,14 +598,15 @@ __global__ __launch_bounds__(kThreads) void k_bias_f32(const BiasPassArgs a) {
           acc[j] = fmaf(x.w, y.w, acc[j]);
         }
       }
-      float z[16], tv[16];
+      float z[16], zu[16], tv[16];
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
-        z[j] = (vb + j < a.V) ? ur[vb + j] + acc[j] : -INFINITY;
+        zu[j] = (vb + j < a.V) ? ur[vb + j] : -INFINITY;
+        z[j] = (MODE == kModeDraft) ? acc[j] : zu[j] + acc[j];  // the draft takes u and b apart
         tv[j] = (kNeedT && vb + j < a.V) ? tr[vb + j] : -INFINITY;
-        if (zrow && vb + j < a.V) zrow[vb + j] = z[j];
+        if (zrow && vb + j < a.V) zrow[vb + j] = zu[j] + acc[j];
       }
-      epilogue<MODE>(st, z, tv, rc, t, t == t_begin, a.seed, kz * tmax[t]);
+      epilogue<MODE>(st, z, tv, rc, t, t == t_begin, a.seed, kz * tmax[t], zu);
     }
   }
   finish<MODE>(st, rc, row, split, a, h == 0);

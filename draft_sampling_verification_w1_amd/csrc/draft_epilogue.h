@@ -47,29 +47,45 @@ struct DraftLane {
   }
 };
 
-// z[j] = logit of token 32 t + 16 h + j of row (r, k) (-inf at or beyond V);
-// `first` marks the first block of the lane's range (the Philox block of
-// four block words is fetched there and at every fourth block).  Exponentials
-// are taken in base 2 with the scaling folded into one fma.  dz bounds the
-// error of every logit of the block; the block's log-mass moves by at most
-// that much (a log of a weighted mean of exp(error)), so it widens the bracket.
-__device__ __forceinline__ void draft_block_epilogue(DraftLane& st, const float* z, int r, int k,
-                                                     int t, bool first, uint64_t seed, float dz) {
+// Logit z[j] = u[j] + b[j] of token 32 t + 16 h + j of row (r, k): u the
+// backbone logit (-inf at or beyond V), b the binary32 bias.  `first` marks the
+// first block of the lane's range (the Philox block of four block words is
+// fetched there and at every fourth block).  dz bounds the contraction error
+// of every bias of the block; a log-sum-exp moves by at most its inputs'
+// largest error, so it widens the bracket.
+//
+// Accuracy of the block's log-mass: exponents are taken in base 2 against the
+// block maximum mt.  The exponent fma(b, L, fma(u, L, -mt2)) (L = log2 e,
+// mt2 = fl(mt L)) is rounded only relative to |z - mt|, never to |z|, and the
+// exact residual mt2_lo = mt L - mt2 of the one rounded product is taken out
+// once per block: log sum_v e^(z_v) = mt + (log2 s - mt2_lo) ln 2, and the
+// block sum enters the running sum as s 2^(-mt2_lo).  What remains is the
+// hardware exp2 / log2 error and the 32-term sum (a few 2^-24 relative).
+__device__ __forceinline__ void draft_block_epilogue(DraftLane& st, const float* u, const float* b,
+                                                     int r, int k, int t, bool first, uint64_t seed,
+                                                     float dz) {
   if (first || (t & 3) == 0) st.words = noise_block(seed, kStreamDraft, r, k, (uint32_t)t >> 2);
-  const float mt = max_halves(max16(z));
+  float zm[16];
+#pragma unroll
+  for (int j = 0; j < 16; ++j) zm[j] = u[j] + b[j];
+  const float mt = max_halves(max16(zm));
   if (mt == -INFINITY) return;  // block without mass
   const float mt2 = mt * kLog2e;
+  const float mt2_lo = fmaf(mt, kLog2e, -mt2);
   float e[16];
 #pragma unroll
-  for (int j = 0; j < 16; ++j) e[j] = __builtin_amdgcn_exp2f(fmaf(z[j], kLog2e, -mt2));
+  for (int j = 0; j < 16; ++j)
+    e[j] = __builtin_amdgcn_exp2f(fmaf(b[j], kLog2e, fmaf(u[j], kLog2e, -mt2)));
   const float s = sum_halves(sum16(e));
+  const float sn = fmaf(s, -mt2_lo * kLn2, s);  // s 2^(-mt2_lo) to first order (|mt2_lo| < 2^-17)
   if (mt > st.M) {
-    st.S = st.S * (double)__builtin_amdgcn_exp2f((st.M - mt) * kLog2e) + (double)s;
+    st.S = st.S * (double)__builtin_amdgcn_exp2f((st.M - mt) * kLog2e) + (double)sn;
     st.M = mt;
   } else {
-    st.S += (double)(s * __builtin_amdgcn_exp2f((mt - st.M) * kLog2e));
+    st.S += (double)(sn * __builtin_amdgcn_exp2f((mt - st.M) * kLog2e));
   }
-  const float sc = fmaf(__builtin_amdgcn_logf(s), kLn2, mt) + gumbel_f32(word_of(st.words, t & 3));
+  const float sc = fmaf(__builtin_amdgcn_logf(s) - mt2_lo, kLn2, mt) +
+                   gumbel_f32(word_of(st.words, t & 3));
   const float d = fmaf(kScoreRel, fabsf(mt), kScoreAbs) + dz;
   st.cand.add(sc - d, sc + d, t);
 }
