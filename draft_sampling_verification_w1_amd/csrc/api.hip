@@ -212,6 +212,9 @@ struct TimingRecord {
 
 std::mutex g_timing_mu;
 bool g_timing_on = false;
+// Set while a call that must not allocate runs on this thread: no timing events
+// are created or recorded for its kernels (creating events can allocate).
+thread_local bool g_no_events = false;
 std::vector<TimingRecord> g_timing_recs;
 std::vector<hipEvent_t> g_event_pool;
 
@@ -239,6 +242,7 @@ void recycle_records() {
 namespace dspark {
 
 TimingScope::TimingScope(const char* name, hipStream_t stream) : slot_(-1), stream_(stream) {
+  if (g_no_events) return;
   std::lock_guard<std::mutex> lock(g_timing_mu);
   if (!g_timing_on) return;
   TimingRecord r{name, pooled_event(), pooled_event(), false};
@@ -257,6 +261,118 @@ TimingScope::~TimingScope() {
 }
 
 }  // namespace dspark
+
+namespace {
+
+// ---- scratch of the no-allocation draft entry point ---------------------------
+// A fixed device array (each GPU the library runs on holds its own copy until
+// the process ends).  Host code never passes the array's name to a kernel: its
+// device address comes from hipGetSymbolAddress, once per device, with that
+// device current.  Calls on one GPU share the array (they must not overlap).
+constexpr size_t kNoAllocScratchBytes = size_t(8) << 20;
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+int noalloc_scratch(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "draft_step_noalloc: current device");
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(DSPARK_ERR_ARG, "draft_step_noalloc: device %d outside [0, %d)", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "draft_step_noalloc: scratch address");
+    if (!ptr || (uintptr_t)ptr % kAlign)
+      return fail(DSPARK_ERR_HIP, "draft_step_noalloc: scratch address not %zu-byte aligned", kAlign);
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return DSPARK_OK;
+}
+
+// ---- the draft stage: argument checks and launch sequence --------------------
+int check_draft_args(const dspark_problem* p, const void* U, const void* W1, const void* W2p,
+                     const int32_t* anchors, const int32_t* tokens, const double* lse,
+                     const double* logq) {
+  if (int e = check_problem(p)) return e;
+  if (!U || !W1 || !W2p || !anchors || !tokens || !lse || !logq)
+    return fail(DSPARK_ERR_ARG, "draft_step: tensor pointers must be non-NULL");
+  if (int e = check_weights(W1, W2p)) return e;
+  return DSPARK_OK;
+}
+
+// Enqueues every draft position; ws holds at least draft_layout(p).bytes.
+int draft_launch(const dspark_problem* p, const void* U, const void* W1, const void* W2p,
+                 const int32_t* anchors, int32_t* tokens, double* lse, double* logq,
+                 float* logpd, void* ws, void* stream) {
+  const bool bf16 = p->dtype == DSPARK_BF16;
+  const DraftLayout L = draft_layout(p);
+  hipStream_t s = (hipStream_t)stream;
+  BiasPassArgs a = {};
+  a.R = p->R;
+  a.gamma = p->gamma;
+  a.V = p->V;
+  a.seed = p->seed;
+  a.nrows = p->R;
+  a.U = U;
+  a.W1 = W1;
+  a.W2p = W2p;
+  a.anchors = anchors;
+  a.tokens = tokens;
+  a.ntiles = (p->V + kTile - 1) / kTile;
+  a.vec_ok = rows_vec_ok(p, U, nullptr);
+  a.tiles_per_stage = L.g.tiles_per_stage;
+  a.nsplit = L.g.nsplit;
+  a.rec_stride = L.g.nsplit;
+  a.pm = at<float>(ws, L.pm);
+  a.ps = at<double>(ws, L.ps);
+  a.cand = cands_at(ws, L.cand);
+  a.zout = logpd;
+  SelectArgs q = {};
+  q.R = p->R;
+  q.gamma = p->gamma;
+  q.V = p->V;
+  q.seed = p->seed;
+  q.ntiles = a.ntiles;
+  q.nsplit = a.nsplit;
+  q.tiles_per_stage = a.tiles_per_stage;
+  q.U = U;
+  q.W1 = W1;
+  q.W2p = W2p;
+  q.anchors = anchors;
+  q.tokens = tokens;
+  q.pm = a.pm;
+  q.ps = a.ps;
+  q.cand = a.cand;
+  q.out_tokens = tokens;
+  q.out_lse = lse;
+  q.out_logq = logq;
+  // bf16: each select writes the drafted tokens' W1 rows as the next
+  // position's matrix-core operands; the first position gathers the anchors'
+  void* bop = bf16 ? at<void>(ws, L.bop) : nullptr;
+  for (int k = 1; k <= p->gamma; ++k) {
+    a.k = k;
+    q.k = k;
+    a.bop = k > 1 ? bop : nullptr;
+    q.bop_out = k < p->gamma ? bop : nullptr;
+    hipError_t e = launch_bias_pass(kModeDraft, bf16, a, s);
+    if (e != hipSuccess) return hip_fail(e, "draft pass");
+    e = launch_select(kSelDraft, bf16, q, s);
+    if (e != hipSuccess) return hip_fail(e, "draft select");
+  }
+  if (logpd) {
+    hipError_t e = launch_logpd(p->R * p->gamma, p->V, lse, logpd, s);
+    if (e != hipSuccess) return hip_fail(e, "draft log p^d");
+  }
+  return ok();
+}
+
+}  // namespace
 
 extern "C" {
 
@@ -331,71 +447,28 @@ __attribute__((visibility("default"))) int dspark_draft_step(
     const dspark_problem* p, const void* U, const void* W1, const void* W2p,
     const int32_t* anchors, int32_t* tokens, double* lse, double* logq, float* logpd, void* ws,
     size_t ws_bytes, void* stream) {
-  if (int e = check_problem(p)) return e;
-  if (!U || !W1 || !W2p || !anchors || !tokens || !lse || !logq)
-    return fail(DSPARK_ERR_ARG, "draft_step: tensor pointers must be non-NULL");
-  if (int e = check_weights(W1, W2p)) return e;
+  if (int e = check_draft_args(p, U, W1, W2p, anchors, tokens, lse, logq)) return e;
   if (int e = check_ws(p, ws, ws_bytes)) return e;
-  const bool bf16 = p->dtype == DSPARK_BF16;
-  const DraftLayout L = draft_layout(p);
-  hipStream_t s = (hipStream_t)stream;
-  BiasPassArgs a = {};
-  a.R = p->R;
-  a.gamma = p->gamma;
-  a.V = p->V;
-  a.seed = p->seed;
-  a.nrows = p->R;
-  a.U = U;
-  a.W1 = W1;
-  a.W2p = W2p;
-  a.anchors = anchors;
-  a.tokens = tokens;
-  a.ntiles = (p->V + kTile - 1) / kTile;
-  a.vec_ok = rows_vec_ok(p, U, nullptr);
-  a.tiles_per_stage = L.g.tiles_per_stage;
-  a.nsplit = L.g.nsplit;
-  a.rec_stride = L.g.nsplit;
-  a.pm = at<float>(ws, L.pm);
-  a.ps = at<double>(ws, L.ps);
-  a.cand = cands_at(ws, L.cand);
-  a.zout = logpd;
-  SelectArgs q = {};
-  q.R = p->R;
-  q.gamma = p->gamma;
-  q.V = p->V;
-  q.seed = p->seed;
-  q.ntiles = a.ntiles;
-  q.nsplit = a.nsplit;
-  q.tiles_per_stage = a.tiles_per_stage;
-  q.U = U;
-  q.W1 = W1;
-  q.W2p = W2p;
-  q.anchors = anchors;
-  q.tokens = tokens;
-  q.pm = a.pm;
-  q.ps = a.ps;
-  q.cand = a.cand;
-  q.out_tokens = tokens;
-  q.out_lse = lse;
-  q.out_logq = logq;
-  // bf16: each select writes the drafted tokens' W1 rows as the next
-  // position's matrix-core operands; the first position gathers the anchors'
-  void* bop = bf16 ? at<void>(ws, L.bop) : nullptr;
-  for (int k = 1; k <= p->gamma; ++k) {
-    a.k = k;
-    q.k = k;
-    a.bop = k > 1 ? bop : nullptr;
-    q.bop_out = k < p->gamma ? bop : nullptr;
-    hipError_t e = launch_bias_pass(kModeDraft, bf16, a, s);
-    if (e != hipSuccess) return hip_fail(e, "draft pass");
-    e = launch_select(kSelDraft, bf16, q, s);
-    if (e != hipSuccess) return hip_fail(e, "draft select");
-  }
-  if (logpd) {
-    hipError_t e = launch_logpd(p->R * p->gamma, p->V, lse, logpd, s);
-    if (e != hipSuccess) return hip_fail(e, "draft log p^d");
-  }
-  return ok();
+  return draft_launch(p, U, W1, W2p, anchors, tokens, lse, logq, logpd, ws, stream);
+}
+
+__attribute__((visibility("default"))) int dspark_draft_step_noalloc(
+    const dspark_problem* p, const void* U, const void* W1, const void* W2p,
+    const int32_t* anchors, int32_t* tokens, double* lse, double* logq, float* logpd,
+    void* stream) {
+  if (int e = check_draft_args(p, U, W1, W2p, anchors, tokens, lse, logq)) return e;
+  const size_t need = draft_layout(p).bytes;
+  if (need > kNoAllocScratchBytes)
+    return fail(DSPARK_ERR_WORKSPACE,
+                "draft_step_noalloc: the problem needs %zu bytes of draft scratch, more than the "
+                "library's fixed %zu (use dspark_draft_step with a workspace)",
+                need, kNoAllocScratchBytes);
+  void* scratch_ptr = nullptr;
+  if (int e = noalloc_scratch(&scratch_ptr)) return e;
+  g_no_events = true;
+  const int e = draft_launch(p, U, W1, W2p, anchors, tokens, lse, logq, logpd, scratch_ptr, stream);
+  g_no_events = false;
+  return e;
 }
 
 __attribute__((visibility("default"))) int dspark_verify(

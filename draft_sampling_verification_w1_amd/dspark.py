@@ -19,7 +19,7 @@ F32, BF16 = 0, 1
 _DTYPES = {torch.float32: F32, torch.bfloat16: BF16}
 
 SYMBOLS = ("dspark_w2_packed_bytes", "dspark_pack_w2", "dspark_workspace_bytes",
-           "dspark_draft_step", "dspark_verify", "dspark_confidence", "dspark_schedule",
+           "dspark_draft_step", "dspark_draft_step_noalloc", "dspark_verify", "dspark_confidence", "dspark_schedule",
            "dspark_schedule_capacity", "dspark_schedule_topk", "dspark_schedule_threshold",
            "dspark_acceptance_stats", "dspark_sts_workspace_bytes", "dspark_sts_fit",
            "dspark_last_error", "dspark_timing_enable",
@@ -57,6 +57,7 @@ def lib() -> ctypes.CDLL:
         L.dspark_workspace_bytes.restype = ctypes.c_size_t
         L.dspark_draft_step.argtypes = [P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                         ctypes.c_size_t, _vp]
+        L.dspark_draft_step_noalloc.argtypes = [P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]
         L.dspark_verify.argtypes = [P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                     _vp, _vp, _vp, ctypes.c_size_t, _vp]
         L.dspark_confidence.argtypes = [P, ctypes.c_int32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]
@@ -77,7 +78,8 @@ def lib() -> ctypes.CDLL:
         L.dspark_last_error.restype = ctypes.c_char_p
         L.dspark_timing_enable.argtypes = [ctypes.c_int]
         L.dspark_timing_report.argtypes = [ctypes.c_char_p, ctypes.c_size_t]
-        for name in ("dspark_pack_w2", "dspark_draft_step", "dspark_verify", "dspark_confidence",
+        for name in ("dspark_pack_w2", "dspark_draft_step", "dspark_draft_step_noalloc",
+                     "dspark_verify", "dspark_confidence",
                      "dspark_schedule", "dspark_schedule_capacity", "dspark_schedule_topk",
                      "dspark_schedule_threshold", "dspark_acceptance_stats", "dspark_sts_fit",
                      "dspark_timing_enable", "dspark_timing_report"):
@@ -166,6 +168,30 @@ def draft_step(U, W1, W2p, anchors, seed: int, ws=None, out=None, logpd=None):
     _check(lib().dspark_draft_step(ctypes.byref(p), _ptr(U), _ptr(W1), _ptr(W2p), _ptr(anchors),
                                    _ptr(tokens), _ptr(lse), _ptr(logq), _ptr(logpd), _ptr(ws),
                                    ws.numel(), _stream()))
+    return tokens, lse, logq
+
+
+def draft_step_noalloc(U, W1, W2p, anchors, seed: int, out, logpd=None):
+    """Stage 1 without a workspace (dspark_draft_step_noalloc): the library's
+    fixed scratch of the current GPU serves the call.  ``out`` = (tokens int32,
+    lse float64, logq float64) [R, gamma], preallocated by the caller."""
+    R, gamma, V = U.shape
+    _need(U, "U")
+    _need(W1, "W1", dtype=U.dtype, shape=(V, 256))
+    _need(W2p, "W2p", dtype=torch.uint8)
+    _need(anchors, "anchors", dtype=torch.int32, shape=(R,))
+    tokens, lse, logq = out
+    _need(tokens, "tokens", dtype=torch.int32, shape=(R, gamma))
+    _need(lse, "lse", dtype=torch.float64, shape=(R, gamma))
+    _need(logq, "logq", dtype=torch.float64, shape=(R, gamma))
+    if logpd is not None:
+        _need(logpd, "logpd", dtype=torch.float32, shape=(R, gamma, V))
+    p = problem(R, gamma, V, U.dtype, seed)
+    if W2p.numel() < w2_packed_bytes(p):
+        raise ValueError("W2p is smaller than dspark_w2_packed_bytes")
+    _check(lib().dspark_draft_step_noalloc(ctypes.byref(p), _ptr(U), _ptr(W1), _ptr(W2p),
+                                           _ptr(anchors), _ptr(tokens), _ptr(lse), _ptr(logq),
+                                           _ptr(logpd), _stream()))
     return tokens, lse, logq
 
 

@@ -117,6 +117,23 @@ int dspark_draft_step(const dspark_problem* p, const void* U, const void* W1, co
                       const int32_t* anchors, int32_t* tokens, double* lse, double* logq,
                       float* logpd, void* ws, size_t ws_bytes, void* stream);
 
+/* dspark_draft_step without a workspace, for callers that cannot allocate
+ * device memory (code under graph capture, tight serving loops, harnesses that
+ * forbid allocation).  Same arguments, outputs and results as
+ * dspark_draft_step; the draft's scratch (split records and the next
+ * position's matrix-core operands) is a fixed 8 MiB device array of the
+ * library instead, one per GPU, held until the process ends.  The call
+ * allocates nothing and records no timing events.  Problems whose draft
+ * scratch exceeds 8 MiB are rejected with DSPARK_ERR_WORKSPACE (every R up to
+ * 8192 fits at V <= 2^20).  The array of the current device is used: calls
+ * that overlap on one GPU (on different streams, or from different threads)
+ * race on it and must be ordered by the caller; a call may start once the
+ * previous call's work on that GPU has been enqueued before it on the same
+ * stream, or has completed.  Nothing in the array needs to start at zero. */
+int dspark_draft_step_noalloc(const dspark_problem* p, const void* U, const void* W1,
+                              const void* W2p, const int32_t* anchors, int32_t* tokens,
+                              double* lse, double* logq, float* logpd, void* stream);
+
 /* Stage 2 -- standard speculative rejection sampling with bonus token, and the
  * analytic acceptance c*.  [P1 요약, §3.2.1; P2 배경]
  * For request r with verify length l_r = lengths[r] (all gamma if lengths is

@@ -142,3 +142,20 @@ def test_sts_validation(L):
     assert lib.dspark_sts_fit(10, 4, fake, None, 8, fake, 15, fake, fake, fake, fake, fake, need, None) == -1
     assert lib.dspark_sts_fit(10, 4, fake, fake, 8, fake, 15, fake, fake, fake, fake, None, need, None) == -4
     assert lib.dspark_sts_fit(10, 4, fake, fake, 8, fake, 15, fake, fake, fake, fake, fake, need - 1, None) == -4
+
+
+def test_noalloc_draft_validation(L):
+    """The no-allocation draft entry point checks its arguments and its scratch
+    size on the host before touching a device."""
+    lib = L.lib()
+    fake = ctypes.c_void_p(0x100000)
+    p = _p(L, dtype=1, R=65536, gamma=1, V=1000)   # 32 MiB of B operands alone
+    assert lib.dspark_draft_step_noalloc(ctypes.byref(p), fake, fake, fake, fake, fake, fake, fake,
+                                        None, None) == -4
+    assert b"scratch" in lib.dspark_last_error()
+    p = _p(L, dtype=1)
+    assert lib.dspark_draft_step_noalloc(ctypes.byref(p), fake, None, fake, fake, fake, fake, fake,
+                                        None, None) == -1
+    p = _p(L, dtype=1, rank=64)
+    assert lib.dspark_draft_step_noalloc(ctypes.byref(p), fake, fake, fake, fake, fake, fake, fake,
+                                        None, None) == -2
