@@ -90,7 +90,9 @@ struct DraftLayout {
 DraftLayout draft_layout(const dspark_problem* p) {
   DraftLayout L;
   L.g = bias_geometry(kModeDraft, p->R, p->V);
-  const size_t n = (size_t)p->R * L.g.nsplit;
+  // the small-batch pass (at most 32 rows, bf16) may use more, tile-granular splits
+  const int ns_small = p->dtype == DSPARK_BF16 ? small_draft_splits(p->R, p->V) : 0;
+  const size_t n = (size_t)p->R * (ns_small > L.g.nsplit ? ns_small : L.g.nsplit);
   Carver c;
   L.pm = c.take(n * sizeof(float));
   L.ps = c.take(n * sizeof(double));
@@ -328,7 +330,12 @@ int draft_launch(const dspark_problem* p, const void* U, const void* W1, const v
   a.vec_ok = rows_vec_ok(p, U, nullptr);
   a.tiles_per_stage = L.g.tiles_per_stage;
   a.nsplit = L.g.nsplit;
-  a.rec_stride = L.g.nsplit;
+  if (const int ns = bf16 ? small_draft_splits(p->R, p->V) : 0) {
+    // at most 32 rows: the small-batch pass, tile-granular splits
+    a.tiles_per_stage = 1;
+    a.nsplit = ns;
+  }
+  a.rec_stride = a.nsplit;
   a.pm = at<float>(ws, L.pm);
   a.ps = at<double>(ws, L.ps);
   a.cand = cands_at(ws, L.cand);

@@ -612,6 +612,131 @@ __global__ __launch_bounds__(kThreads) void k_bias_f32(const BiasPassArgs a) {
   finish<MODE>(st, rc, row, split, a, h == 0);
 }
 
+// Draft pass for at most 32 rows (one 32-row group, bf16): with a single row
+// group nothing is worth sharing between waves, so every wave streams its own
+// contiguous quarter of the workgroup's tiles with no LDS staging and no
+// barrier: the A operands (packed W2 tile) and the lane's 16 backbone logits
+// are loaded straight into registers, one tile ahead, and each W2 tile crosses
+// the fabric once per position.  Workgroup = split (tile-granular); the four
+// waves' states of each row are merged through LDS at the end.
+template <bool VEC, bool ZOUT>
+__global__ __launch_bounds__(256) void k_bias_small(const BiasPassArgs a) {
+  constexpr int kW = 4;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int n = lane & 31;
+  const int h = lane >> 5;
+  const int split = blockIdx.x;
+  const int t0 = split_tile(split, a.nsplit, a.ntiles, 1);
+  const int t1 = split_tile(split + 1, a.nsplit, a.ntiles, 1);
+  const int per = (t1 - t0 + kW - 1) / kW;
+  const int tb = min(t1, t0 + wave * per);
+  const int te = min(t1, tb + per);
+  const bool bop_ready = a.bop != nullptr;
+  const RowCtx rc = row_ctx(a, n, a.nrows, true, a.k, !bop_ready);
+  LaneState<kModeDraft> st;
+  st.init();
+
+  bf16x8 bop[kSteps];
+  if (bop_ready) {
+    const u32x4* src = reinterpret_cast<const u32x4*>(a.bop) + bop_chunk(n, 0, h);
+#pragma unroll
+    for (int s = 0; s < kSteps; ++s) {
+      const u32x4 v = src[s * 64];
+      bop[s] = as_bf16x8(rc.active ? v : (u32x4){0u, 0u, 0u, 0u});
+    }
+  } else {
+    const u32x4* w1 = reinterpret_cast<const u32x4*>(
+        reinterpret_cast<const uint16_t*>(a.W1) + (int64_t)rc.prev * kRank + 128 * h);
+#pragma unroll
+    for (int s = 0; s < kSteps; ++s) bop[s] = as_bf16x8(rc.active ? w1[s] : (u32x4){0u, 0u, 0u, 0u});
+  }
+  float n1 = 0.f;
+#pragma unroll
+  for (int s = 0; s < kSteps; ++s) {
+    const u32x4 v = __builtin_bit_cast(u32x4, bop[s]);
+    n1 += (fabsf(bf16_lo(v.x)) + fabsf(bf16_hi(v.x))) + (fabsf(bf16_lo(v.y)) + fabsf(bf16_hi(v.y))) +
+          (fabsf(bf16_lo(v.z)) + fabsf(bf16_hi(v.z))) + (fabsf(bf16_lo(v.w)) + fabsf(bf16_hi(v.w)));
+  }
+  const float kz = kContractErr * sum_halves(n1);
+  const float* tmax = w2_tile_absmax(a.W2p, true, a.ntiles);
+  const u32x4* W2q = reinterpret_cast<const u32x4*>(a.W2p);
+  const uint16_t* urow = rc.active ? reinterpret_cast<const uint16_t*>(rc.urow) : nullptr;
+  float* zrow = nullptr;
+  if constexpr (ZOUT)
+    if (rc.active) zrow = a.zout + ((int64_t)rc.r * a.gamma + (rc.k - 1)) * (int64_t)a.V;
+
+  // tile loads: 16 A fragments and the lane's 16 logits (tiles past the
+  // wave's range repeat its last tile and are never used)
+  auto load_tile = [&](int t, u32x4* A, u32x4& ulo, u32x4& uhi) {
+    const int tt = min(t, max(te - 1, tb));
+#pragma unroll
+    for (int s = 0; s < kSteps; ++s) A[s] = gload16(W2q + (int64_t)tt * 1024 + s * 64 + lane);
+    const int v = tt * kTile + 16 * h;
+    if (VEC && urow != nullptr && v + 16 <= a.V) {
+      ulo = gload16(urow + v);
+      uhi = gload16(urow + v + 8);
+    } else {
+      ulo = chunk_load(urow, v, a.V);
+      uhi = chunk_load(urow, v + 8, a.V);
+    }
+  };
+  u32x4 A[kSteps], ulo, uhi;
+  if (tb < te) load_tile(tb, A, ulo, uhi);
+  for (int t = tb; t < te; ++t) {
+    u32x4 An[kSteps], nlo, nhi;
+    load_tile(t + 1, An, nlo, nhi);  // one tile ahead
+    f32x16 acc;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) acc[j] = 0.f;
+#pragma unroll
+    for (int s = 0; s < kSteps; ++s)
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(A[s]), bop[s], acc, 0, 0, 0);
+    float z[16], zu[16];
+    decode16(ulo, uhi, zu);
+#pragma unroll
+    for (int j = 0; j < 16; ++j) z[j] = acc[j];
+    if constexpr (ZOUT) {
+      const int vb = t * kTile + 16 * h;
+      if (zrow)
+#pragma unroll
+        for (int j = 0; j < 16; ++j)
+          if (vb + j < a.V) zrow[vb + j] = zu[j] + z[j];
+    }
+    draft_block_epilogue(st, zu, z, rc.r, rc.k, t, t == tb, a.seed, kz * tmax[t]);
+#pragma unroll
+    for (int s = 0; s < kSteps; ++s) A[s] = An[s];
+    ulo = nlo;
+    uhi = nhi;
+  }
+
+  // merge the four waves' states of each row (disjoint tile ranges)
+  __shared__ float sm[kW][32], slo[kW][32], shi1[kW][32], shi2[kW][32];
+  __shared__ double ss[kW][32];
+  __shared__ int sb1[kW][32];
+  if (h == 0) {
+    sm[wave][n] = st.M;
+    ss[wave][n] = st.S;
+    slo[wave][n] = st.cand.lo;
+    shi1[wave][n] = st.cand.hi1;
+    shi2[wave][n] = st.cand.hi2;
+    sb1[wave][n] = st.cand.b1;
+  }
+  __syncthreads();
+  if (wave == 0) {
+    for (int w = 1; w < kW; ++w) {
+      lse_merge(st.M, st.S, sm[w][n], ss[w][n]);
+      CandState o;
+      o.lo = slo[w][n];
+      o.hi1 = shi1[w][n];
+      o.hi2 = shi2[w][n];
+      o.b1 = sb1[w][n];
+      st.cand.merge(o);
+    }
+    finish<kModeDraft>(st, rc, n, split, a, h == 0);
+  }
+}
+
 }  // namespace
 
 // Vocabulary splits: enough workgroups for one full round on MI355X (256 CUs,
@@ -628,11 +753,23 @@ BiasGeometry bias_geometry(int mode, int nrows, int V) {
   return g;
 }
 
+int small_draft_splits(int nrows, int V) {
+  const int ntiles = (V + kTile - 1) / kTile;
+  return nrows <= 32 ? min(ntiles, 256) : 0;
+}
+
 hipError_t launch_bias_pass(int mode, bool bf16, const BiasPassArgs& a, hipStream_t stream) {
   TimingScope timing(mode == kModeDraft ? "draft_bias" : (mode == kModeCstar ? "cstar_bias" : "residual_bias"), stream);
   const dim3 grid(a.nsplit, (a.nrows + kRowsPerBlock - 1) / kRowsPerBlock);
   const dim3 block(kThreads);
-  if (bf16 && mode == kModeDraft && a.zout) {
+  if (bf16 && mode == kModeDraft && a.tiles_per_stage == 1) {  // at most 32 rows
+    if (a.nrows > 32) return hipErrorInvalidValue;
+    const dim3 g(a.nsplit), b(256);
+    if (a.vec_ok && a.zout) hipLaunchKernelGGL((k_bias_small<true, true>), g, b, 0, stream, a);
+    else if (a.vec_ok) hipLaunchKernelGGL((k_bias_small<true, false>), g, b, 0, stream, a);
+    else if (a.zout) hipLaunchKernelGGL((k_bias_small<false, true>), g, b, 0, stream, a);
+    else hipLaunchKernelGGL((k_bias_small<false, false>), g, b, 0, stream, a);
+  } else if (bf16 && mode == kModeDraft && a.zout) {
     if (a.vec_ok) hipLaunchKernelGGL((k_bias_bf16<kModeDraft, 2, true, true>), grid, block, 0, stream, a);
     else hipLaunchKernelGGL((k_bias_bf16<kModeDraft, 2, false, true>), grid, block, 0, stream, a);
   } else if (bf16 && a.vec_ok) {
