@@ -515,8 +515,11 @@ __global__ __launch_bounds__(kThreads) void k_bias_f32(const BiasPassArgs a) {
   if (active_rows - row0 <= 32) {
     // At most one wave's rows: the 8 waves share them and split the rank
     // instead, wave w summing ranks [32w, 32w + 32); wave 0 adds the eight
-    // partial sums in a fixed order and runs the epilogue.
+    // partial sums in a fixed order and runs the epilogue.  Each tile's slice
+    // of the transposed W2 (32 tokens x 256, 32 KB) is staged in LDS with one
+    // coalesced load per thread quad, the next tile's slice in flight meanwhile.
     __shared__ float part[kWaves][16][64];
+    __shared__ f32x4 sW[2][kTile * (kRank / 4)];
     const int row = row0 + n;
     const RowCtx rc = row_ctx(a, row, active_rows, false, a.k);
     LaneState<MODE> st;
@@ -529,17 +532,34 @@ __global__ __launch_bounds__(kThreads) void k_bias_f32(const BiasPassArgs a) {
     float* zrow = (MODE == kModeDraft && a.zout && rc.active)
                       ? a.zout + ((int64_t)rc.r * a.gamma + (rc.k - 1)) * (int64_t)a.V
                       : nullptr;
+    f32x4 xw[8];  // this wave's 32 ranks of the row's W1 operand
+#pragma unroll
+    for (int q = 0; q < 8; ++q) xw[q] = rc.active ? w1[8 * wave + q] : (f32x4){0.f, 0.f, 0.f, 0.f};
+    constexpr int kSlice = kTile * (kRank / 4);        // 2048 f32x4 per tile
+    constexpr int kPer = kSlice / kThreads;             // 4 per thread
+    f32x4 pre[kPer];
+    auto load_slice = [&](int t) {
+#pragma unroll
+      for (int q = 0; q < kPer; ++q) pre[q] = W2T[(int64_t)t * kSlice + tid + q * kThreads];
+    };
+    if (t_begin < t_end) load_slice(t_begin);
     for (int t = t_begin; t < t_end; ++t) {
+      const int buf = (t - t_begin) & 1;
+#pragma unroll
+      for (int q = 0; q < kPer; ++q) sW[buf][tid + q * kThreads] = pre[q];
+      if (t + 1 < t_end) load_slice(t + 1);
+      stage_barrier();  // the slice is visible; the loads of the next stay in flight
       const int vb = t * kTile + 16 * h;
       float acc[16];
 #pragma unroll
       for (int j = 0; j < 16; ++j) acc[j] = 0.f;
       if (rc.active) {
-        for (int i4 = 8 * wave; i4 < 8 * wave + 8; ++i4) {
-          const f32x4 x = w1[i4];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          const f32x4 x = xw[q];
 #pragma unroll
           for (int j = 0; j < 16; ++j) {
-            const f32x4 y = W2T[(int64_t)(vb + j) * (kRank / 4) + i4];
+            const f32x4 y = sW[buf][(16 * h + j) * (kRank / 4) + 8 * wave + q];
             acc[j] = fmaf(x.x, y.x, acc[j]);
             acc[j] = fmaf(x.y, y.y, acc[j]);
             acc[j] = fmaf(x.z, y.z, acc[j]);
@@ -549,7 +569,7 @@ __global__ __launch_bounds__(kThreads) void k_bias_f32(const BiasPassArgs a) {
       }
 #pragma unroll
       for (int j = 0; j < 16; ++j) part[wave][j][lane] = acc[j];
-      __syncthreads();
+      stage_barrier();  // LDS only: the next slice's loads stay in flight
       if (wave == 0) {
         float z[16], zu[16], tv[16];
 #pragma unroll
@@ -563,7 +583,7 @@ __global__ __launch_bounds__(kThreads) void k_bias_f32(const BiasPassArgs a) {
         }
         epilogue<MODE>(st, z, tv, rc, t, t == t_begin, a.seed, kz * tmax[t], zu);
       }
-      __syncthreads();
+      stage_barrier();
     }
     if (wave == 0) finish<MODE>(st, rc, row, split, a, h == 0);
     return;
