@@ -33,16 +33,18 @@ def _run_case(dspark, cfg, lengths=None, check_schedule=True, inp=None):
     U, W1, W2 = to_dev(inp["U"]), to_dev(inp["W1"]), to_dev(inp["W2"])
     anchors = to_dev(inp["anchors"])
     W2p = dspark.pack_w2(W2, cfg.V)
-    lp = torch.empty((cfg.R, cfg.gamma, cfg.V), dtype=torch.float32, device="cuda")
-    tok, lse, logq = dspark.draft_step(U, W1, W2p, anchors, cfg.seed, logpd=lp)
+    tok, lse, logq = dspark.draft_step(U, W1, W2p, anchors, cfg.seed)
     torch.cuda.synchronize()
     tok_h = tok.cpu().numpy()
     n, ties = compare_draft(od, tok_h, lse.cpu().numpy(), logq.cpu().numpy())
+    # with the log p^d output the draft runs position by position: same draws
+    lp = torch.empty((cfg.R, cfg.gamma, cfg.V), dtype=torch.float32, device="cuda")
+    res = dspark.draft_step(U, W1, W2p, anchors, cfg.seed, logpd=lp)
+    for x, y in zip(res, (tok, lse, logq)):
+        assert torch.equal(x, y), "the draft with the log p^d output differs"
     rows = compare_logpd(lp.cpu().numpy(), inp["U"], inp["W1"], O.to_f64(inp["W2"]),
                          inp["anchors"], tok_h, od)
     log(f"  draft: {n} positions compared, {ties} near-ties; log p^d of {rows} rows")
-    tok0 = dspark.draft_step(U, W1, W2p, anchors, cfg.seed)[0]
-    assert torch.equal(tok0, tok), "the log p^d output changed the drafted tokens"
 
     T = build_target(cfg, inp, od["tokens"])
     ov = O.verify(inp["U"], inp["W1"], inp["W2"], inp["anchors"], od["tokens"], T, lengths, cfg.seed)
