@@ -367,6 +367,7 @@ int draft_launch(const dspark_problem* p, const void* U, const void* W1, const v
     q.k = k;
     a.bop = k > 1 ? bop : nullptr;
     q.bop_out = k < p->gamma ? bop : nullptr;
+    q.bop_in = a.bop;
     hipError_t e = launch_bias_pass(kModeDraft, bf16, a, s);
     if (e != hipSuccess) return hip_fail(e, "draft pass");
     e = launch_select(kSelDraft, bf16, q, s);

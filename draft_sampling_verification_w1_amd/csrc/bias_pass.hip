@@ -132,6 +132,12 @@ typedef __attribute__((address_space(1))) const u32x4 global_u32x4;
 __device__ __forceinline__ u32x4 gload16(const void* p) {
   return *(global_u32x4*)(p);
 }
+// The same with the nontemporal hint: rows read once (measured on MI355X: the
+// c* and residual passes, which stream both U and T, gain ~3%; the draft,
+// which streams U beside the re-read W2 tiles, does not).
+__device__ __forceinline__ u32x4 gload16_nt(const void* p) {
+  return __builtin_nontemporal_load((global_u32x4*)(p));
+}
 
 // ||W1[x]||_1 of a binary32 row (64 16-byte chunks).
 __device__ __forceinline__ float w1_norm1(const f32x4* w1) {
@@ -313,7 +319,9 @@ __device__ void bias_body(const BiasPassArgs& a, int split, int nsplit, int row_
   auto row_seg = [&](const uint16_t* r, int v, bool live) -> u32x4 {
     if constexpr (VEC) {
       const bool in = live && r != nullptr && v + 8 <= a.V;
-      return gload16(in ? static_cast<const void*>(r + v) : static_cast<const void*>(kNegInfBf16x8));
+      const void* src = in ? static_cast<const void*>(r + v) : static_cast<const void*>(kNegInfBf16x8);
+      if constexpr (kNeedT) return gload16_nt(src);
+      else return gload16(src);
     } else {
       return live ? chunk_load(r, v, a.V) : gload16(kNegInfBf16x8);
     }

@@ -163,6 +163,7 @@ struct SelectArgs {
   BlockCands cand_f;
   const float* wpos;
   void* bop_out;              // draft, bf16: B operands for the next position (bop_chunk order) or null
+  const void* bop_in;         // draft, bf16: this position's B operands (written by the previous select) or null
   int32_t* out_tokens;        // draft: tokens [R, gamma]; residual / bonus: out_token [R]
   double* out_lse;            // draft
   double* out_logq;           // draft

@@ -196,10 +196,20 @@ __device__ void select_row(const SelectArgs& a, int bf16_flag, int i, SelShared&
     }
   }
   if constexpr (kBias) {
-    const int x = (q.k == 1) ? a.anchors[q.r] : a.tokens[(int64_t)q.r * a.gamma + (q.k - 2)];
-    q.prev = min(max(x, 0), a.V - 1);
     q.uoff = ((int64_t)q.r * a.gamma + (q.k - 1)) * a.V;
-    if (tid < kRank) w1s[tid] = stored(a.W1, bf16, (int64_t)q.prev * kRank + tid);
+    if (kDraft && a.bop_in != nullptr) {
+      // the previous select left W1[x_{k-1}] as this row's B operands: one load
+      // instead of the token and then its row
+      if (tid < kRank) {
+        const int c = tid >> 3;  // 16-byte chunk c = 16h + s holds elements [8c, 8c + 8)
+        const uint16_t* chunk = reinterpret_cast<const uint16_t*>(a.bop_in) + bop_chunk(q.r, c & 15, c >> 4) * 8;
+        w1s[tid] = (double)bf16_at(chunk, tid & 7);
+      }
+    } else {
+      const int x = (q.k == 1) ? a.anchors[q.r] : a.tokens[(int64_t)q.r * a.gamma + (q.k - 2)];
+      q.prev = min(max(x, 0), a.V - 1);
+      if (tid < kRank) w1s[tid] = stored(a.W1, bf16, (int64_t)q.prev * kRank + tid);
+    }
   }
   const int64_t rec0 = (int64_t)q.rec * a.nsplit;
   const uint32_t sblock = kDraft ? kStreamDraft : (kResid ? kStreamResidual : kStreamBonus);
