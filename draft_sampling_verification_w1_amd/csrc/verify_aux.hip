@@ -119,23 +119,31 @@ __global__ __launch_bounds__(256) void k_target_lse(int gamma, int V, const E* T
   const int v0 = split * chunk;
   const int v1 = min(V, v0 + chunk);
   const bool vec_ok = w.vec_ok != 0;
-  float m = -INFINITY;
+  // Running max m and s = sum exp(x - m).  Each exponent is one fma,
+  // fma(x, L, -m2) with m2 = fl(m L) (L = log2 e): rounded relative to
+  // |x - m| only; the exact residual lo = m L - m2 of the one rounded product
+  // is taken out of every chunk sum as the factor 2^-lo ~ 1 - lo ln 2.
+  float m = -INFINITY, m2 = 0.f, corr = 1.f;
   double s = 0.0;
-  for (int v = v0 + 8 * threadIdx.x; v < v1; v += 8 * 256) {
-    float x[8];
-    load8(row, v, v1, vec_ok, x);
+  for (int v = v0 + 16 * threadIdx.x; v < v1; v += 16 * 256) {
+    float x[16];
+    load16(row, v, v1, vec_ok, x);
     float mt = x[0];
 #pragma unroll
-    for (int j = 1; j < 8; ++j) mt = fmaxf(mt, x[j]);
+    for (int j = 1; j < 16; ++j) mt = fmaxf(mt, x[j]);
     if (mt > m) {
       if (m != -INFINITY) s *= exp((double)m - (double)mt);
       m = mt;
+      m2 = m * kLog2e;
+      corr = fmaf(-fmaf(m, kLog2e, -m2), kLn2, 1.f);
     }
     if (m != -INFINITY) {
-      float e[8];
+      float e[16];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) e[j] = __builtin_amdgcn_exp2f((x[j] - m) * kLog2e);
-      s += (double)(((e[0] + e[1]) + (e[2] + e[3])) + ((e[4] + e[5]) + (e[6] + e[7])));
+      for (int j = 0; j < 16; ++j) e[j] = __builtin_amdgcn_exp2f(fmaf(x[j], kLog2e, -m2));
+      const float a0 = ((e[0] + e[1]) + (e[2] + e[3])) + ((e[4] + e[5]) + (e[6] + e[7]));
+      const float a1 = ((e[8] + e[9]) + (e[10] + e[11])) + ((e[12] + e[13]) + (e[14] + e[15]));
+      s += (double)((a0 + a1) * corr);
     }
   }
   block_lse(m, s);
