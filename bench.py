@@ -173,6 +173,36 @@ def calibrate_copy(mb):
     log(f"[bench] copy calibration: 3 copies of {mb} MiB")
 
 
+def memory_probe(reps=30):
+    """Read bandwidth against working-set size: a float32 buffer of S MiB summed
+    by torch (one read of every byte) many times in a row; sizes within the
+    256 MB Infinity Cache against sizes well beyond it.  One JSON line."""
+    import torch
+    out = []
+    for mib in (32, 64, 128, 192, 256, 384, 1024, 4096):
+        buf = torch.ones(mib << 18, dtype=torch.float32, device="cuda")
+        for _ in range(3):
+            buf.sum()
+        times = []
+        for _ in range(reps if mib <= 1024 else max(5, reps // 4)):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            buf.sum()
+            e1.record()
+            e1.synchronize()
+            times.append(e0.elapsed_time(e1))
+        times.sort()
+        med = times[len(times) // 2]
+        out.append({"MiB": mib, "median_us": round(med * 1e3, 1),
+                    "GB_per_s_median": round((mib << 20) / (med * 1e-3) / 1e9, 1),
+                    "GB_per_s_best": round((mib << 20) / (times[0] * 1e-3) / 1e9, 1)})
+        log(f"[bench] memory probe {mib} MiB: median {med * 1e3:.1f} us, "
+            f"{out[-1]['GB_per_s_median']:.0f} GB/s")
+        del buf
+    return {"probe": "read bandwidth vs working set (torch.sum of a float32 buffer, repeated)",
+            "sizes": out}
+
+
 def cpu_model():
     """The host CPU's model name (first 'model name' of /proc/cpuinfo)."""
     try:
@@ -422,6 +452,8 @@ def main():
                          "--calibrate-copy 1024)")
     ap.add_argument("--rounds", type=int, default=0,
                     help="run this many rounds of multi-round decoding instead (one JSON line)")
+    ap.add_argument("--memory-probe", action="store_true",
+                    help="measure read bandwidth against working-set size instead (one JSON line)")
     ap.add_argument("--scheduler-variants", action="store_true",
                     help="time the production scheduler, static threshold and acceptance "
                          "statistics instead of the round (one JSON line of its own)")
@@ -448,6 +480,9 @@ def main():
     dspark.lib()
     if args.calibrate_copy:
         calibrate_copy(args.calibrate_copy)
+    if args.memory_probe:
+        print(json.dumps(memory_probe()), flush=True)
+        return
     if args.scheduler_variants:
         print(json.dumps(scheduler_variants(cfg, dspark, synth, args.steps, args.warmup)), flush=True)
         return

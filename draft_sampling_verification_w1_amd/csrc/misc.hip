@@ -30,24 +30,33 @@ __global__ __launch_bounds__(256) void k_pack_w2_bf16(int V, int ntiles, const u
   out[g] = (u32x4){w[0], w[1], w[2], w[3]};
 }
 
-// Largest |W2[i][v]| over the rank and the 32 tokens of each tile (tokens
-// below V), one workgroup per tile: the per-tile factor of the contraction's
-// error bound that the split passes use to bracket their binary32 scores.
-template <typename E>
-__global__ __launch_bounds__(kRank) void k_tile_absmax(int V, const E* W2, float* tmax) {
-  __shared__ float part[kRank / 64];
+// Largest |W2[i][v]| over the rank and the 32 tokens of each tile: the
+// per-tile factor of the contraction's error bound that the split passes use
+// to bracket their binary32 scores.  Read from the packed tiles (contiguous:
+// 16 KB bf16, 32 KB binary32), whose entries for tokens at or beyond V are
+// zeros and never raise it; one workgroup per tile, after the packing kernel.
+template <bool BF16>
+__global__ __launch_bounds__(256) void k_tile_absmax(const u32x4* W2p, float* tmax) {
+  constexpr int kChunks = BF16 ? kSteps * 64 : kTile * kRank / 4;  // 16-byte chunks per tile
+  __shared__ float part[4];
   const int t = blockIdx.x;
-  const int i = threadIdx.x;  // rank index
+  const u32x4* tile = W2p + (int64_t)t * kChunks;
   float m = 0.f;
-  for (int j = 0; j < kTile; ++j) {
-    const int v = t * kTile + j;
-    if (v < V) m = fmaxf(m, fabsf(elem_at(W2, (int64_t)i * V + v)));
+#pragma unroll
+  for (int c = threadIdx.x; c < kChunks; c += 256) {
+    const u32x4 q = tile[c];
+    const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      if constexpr (BF16) m = fmaxf(m, fmaxf(fabsf(bf16_lo(w[e])), fabsf(bf16_hi(w[e]))));
+      else m = fmaxf(m, fabsf(__uint_as_float(w[e])));
+    }
   }
 #pragma unroll
   for (int off = 1; off < 64; off <<= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
-  if ((i & 63) == 0) part[i >> 6] = m;
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = m;
   __syncthreads();
-  if (i == 0) tmax[t] = fmaxf(fmaxf(part[0], part[1]), fmaxf(part[2], part[3]));
+  if (threadIdx.x == 0) tmax[t] = fmaxf(fmaxf(part[0], part[1]), fmaxf(part[2], part[3]));
 }
 
 // Transposed f32 W2: out[v][i] = W2[i][v], zero rows for v >= V.
@@ -127,14 +136,14 @@ hipError_t launch_pack_w2(bool bf16, int V, const void* W2, void* W2p, hipStream
     const int64_t n = (int64_t)ntiles * kSteps * 64;
     hipLaunchKernelGGL(k_pack_w2_bf16, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, V,
                        ntiles, (const uint16_t*)W2, (u32x4*)W2p);
-    hipLaunchKernelGGL(k_tile_absmax<uint16_t>, dim3(ntiles), dim3(kRank), 0, stream, V,
-                       (const uint16_t*)W2, tmax);
+    hipLaunchKernelGGL(k_tile_absmax<true>, dim3(ntiles), dim3(256), 0, stream,
+                       (const u32x4*)W2p, tmax);
   } else {
     const int64_t n = (int64_t)ntiles * kTile * kRank;
     hipLaunchKernelGGL(k_pack_w2_f32, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, V,
                        ntiles * kTile, (const float*)W2, (float*)W2p);
-    hipLaunchKernelGGL(k_tile_absmax<float>, dim3(ntiles), dim3(kRank), 0, stream, V,
-                       (const float*)W2, tmax);
+    hipLaunchKernelGGL(k_tile_absmax<false>, dim3(ntiles), dim3(256), 0, stream,
+                       (const u32x4*)W2p, tmax);
   }
   return hipGetLastError();
 }
