@@ -127,14 +127,17 @@ def write_traffic(fetch_csv, write_csv, copy_mib, commands):
     def load(path):
         per = {}
         with open(path) as f:
-            for row in csv.DictReader(f):
-                per.setdefault(row["Kernel_Name"], []).append(float(row["Counter_Value"]))
+            rows = sorted(csv.DictReader(f), key=lambda r: int(r["Dispatch_Id"]))
+        for row in rows:
+            per.setdefault(row["Kernel_Name"], []).append(float(row["Counter_Value"]))
         return per
 
     fetch, write = load(fetch_csv), load(write_csv)
+    # the calibration copies are the process's first three device copies (later
+    # copies, e.g. the cold-cache flushes, are not calibrated sizes)
     copy_bytes = 3 * copy_mib * 2 ** 20
-    fetch_scale = copy_bytes / (sum(fetch["__amd_rocclr_copyBuffer"]) * 1024)
-    write_scale = copy_bytes / (sum(write["__amd_rocclr_copyBuffer"]) * 1024)
+    fetch_scale = copy_bytes / (sum(fetch["__amd_rocclr_copyBuffer"][:3]) * 1024)
+    write_scale = copy_bytes / (sum(write["__amd_rocclr_copyBuffer"][:3]) * 1024)
     out = {"command_fetch": commands[0], "command_write": commands[1],
            "fetch_scale": fetch_scale, "write_scale": write_scale, "kernels": {}}
     print("| kernel | dispatches | FETCH_SIZE KiB/dispatch | WRITE_SIZE KiB/dispatch | "
@@ -461,7 +464,7 @@ def main():
     if args.write_traffic:
         cmd = ("cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc {c} --output-format csv -d "
                "$REPO/gpurun_out/prof/{d} -o bench -- python3 $REPO/bench.py --steps 2 --warmup 1 "
-               "--no-cpu-baseline --calibrate-copy 1024")
+               "--no-cpu-baseline --cold-steps 5 --calibrate-copy 1024")
         write_traffic(args.write_traffic[0], args.write_traffic[1], 1024,
                       (cmd.format(c="FETCH_SIZE", d="fetch"), cmd.format(c="WRITE_SIZE", d="write")))
         return
