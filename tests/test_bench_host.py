@@ -42,6 +42,26 @@ def test_write_traffic_scales_by_the_copy(tmp_path, monkeypatch):
     assert bench.measured_traffic("draft_bias") == k["bytes_per_launch"]
 
 
+def test_write_traffic_calibrates_on_the_first_three_copies(tmp_path, monkeypatch):
+    # later device copies (cold-cache flushes of another size) and a file whose
+    # rows are not in dispatch order leave the scales at those of the first three
+    draft = "void dspark::(anonymous namespace)::k_bias_bf16<0, 2, true, false>(dspark::BiasPassArgs)"
+    rows = [("__amd_rocclr_copyBuffer", 512.0)] * 3 + [(draft, 1000.0), ("__amd_rocclr_copyBuffer", 9999.0)]
+    for path, counter, rr in ((tmp_path / "f.csv", "FETCH_SIZE", rows),
+                              (tmp_path / "w.csv", "WRITE_SIZE",
+                               [(n, 2 * v) for n, v in rows])):
+        with open(path, "w", newline="") as f:
+            w = csv.DictWriter(f, fieldnames=FIELDS)
+            w.writeheader()
+            for i in reversed(range(len(rr))):  # written last dispatch first
+                w.writerow({"Dispatch_Id": i, "Kernel_Name": rr[i][0], "Counter_Name": counter,
+                            "Counter_Value": rr[i][1]})
+    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(tmp_path / "traffic.json"))
+    bench.write_traffic(str(tmp_path / "f.csv"), str(tmp_path / "w.csv"), 1, ("f", "w"))
+    t = json.load(open(tmp_path / "traffic.json"))
+    assert t["fetch_scale"] == pytest.approx(2.0) and t["write_scale"] == pytest.approx(1.0)
+
+
 def test_algorithmic_bytes_of_the_high_concurrency_round():
     from draft_sampling_verification_w1_amd import synth
     cfg = synth.CONFIGS["high_concurrency"]
