@@ -139,6 +139,14 @@ __device__ __forceinline__ u32x4 gload16_nt(const void* p) {
   return __builtin_nontemporal_load((global_u32x4*)(p));
 }
 
+// max|W2| of tile t (t uniform across the wave), read through the scalar
+// cache.  A vector load here would count against vmcnt behind the stage
+// prefetch: since that counter retires in order, waiting for the value before
+// each tile's epilogue would drain every stage still in flight.
+__device__ __forceinline__ float tile_absmax(const float* tmax, int t) {
+  return ((const __attribute__((address_space(4))) float*)tmax)[__builtin_amdgcn_readfirstlane(t)];
+}
+
 // ||W1[x]||_1 of a binary32 row (64 16-byte chunks).
 __device__ __forceinline__ float w1_norm1(const f32x4* w1) {
   float n1 = 0.f;
@@ -420,7 +428,7 @@ __device__ void bias_body(const BiasPassArgs& a, int split, int nsplit, int row_
             // backbone logits are added after it; c* (no bracket) seeds the
             // accumulator with them, so that the chain yields z = U + B
             const int s0 = 4 * tau + 2 * h;
-            const float dz = kz * tmax[t];
+            const float dz = kz * tile_absmax(tmax, t);
             f32x16 acc;
             if constexpr (MODE == kModeCstar) {
               float zu[16];
@@ -589,7 +597,7 @@ __global__ __launch_bounds__(kThreads) void k_bias_f32(const BiasPassArgs a) {
           tv[j] = (kNeedT && rc.active && vb + j < a.V) ? tr[vb + j] : -INFINITY;
           if (zrow && vb + j < a.V) zrow[vb + j] = zu[j] + b;
         }
-        epilogue<MODE>(st, z, tv, rc, t, t == t_begin, a.seed, kz * tmax[t], zu);
+        epilogue<MODE>(st, z, tv, rc, t, t == t_begin, a.seed, kz * tile_absmax(tmax, t), zu);
       }
       stage_barrier();
     }
@@ -634,7 +642,7 @@ __global__ __launch_bounds__(kThreads) void k_bias_f32(const BiasPassArgs a) {
         tv[j] = (kNeedT && vb + j < a.V) ? tr[vb + j] : -INFINITY;
         if (zrow && vb + j < a.V) zrow[vb + j] = zu[j] + acc[j];
       }
-      epilogue<MODE>(st, z, tv, rc, t, t == t_begin, a.seed, kz * tmax[t], zu);
+      epilogue<MODE>(st, z, tv, rc, t, t == t_begin, a.seed, kz * tile_absmax(tmax, t), zu);
     }
   }
   finish<MODE>(st, rc, row, split, a, h == 0);
@@ -731,7 +739,7 @@ __global__ __launch_bounds__(256) void k_bias_small(const BiasPassArgs a) {
         for (int j = 0; j < 16; ++j)
           if (vb + j < a.V) zrow[vb + j] = zu[j] + z[j];
     }
-    draft_block_epilogue(st, zu, z, rc.r, rc.k, t, t == tb, a.seed, kz * tmax[t]);
+    draft_block_epilogue(st, zu, z, rc.r, rc.k, t, t == tb, a.seed, kz * tile_absmax(tmax, t));
 #pragma unroll
     for (int s = 0; s < kSteps; ++s) A[s] = An[s];
     ulo = nlo;
