@@ -12,7 +12,7 @@
 //
 // bf16 rows use the gfx950 matrix cores.  A workgroup owns 256 rows (8 waves x
 // 32 rows) and a contiguous range of 32-token tiles, taken two tiles (64
-// tokens) per pipeline stage.  Each wave prefetches several stages ahead into
+// tokens) per pipeline stage.  Each wave prefetches two stages ahead into
 // registers and writes a stage to LDS just before it is used: the packed W2
 // tiles (the MFMA A operand, shared by all 8 waves, so each W2 byte crosses
 // L2 -> CU once per workgroup) and 128-byte segments of the wave's own rows of
@@ -21,9 +21,14 @@
 // the B operand, held in registers for the whole pass; v_mfma_f32_32x32x16_bf16
 // accumulates in fp32.  The packed tile order
 // makes lane (n, h) own tokens [16h, 16h+16) of row n, so a 32-token block is
-// the lane pair (n, n+32).  The chain accumulates B from zero and the backbone
-// logits are added to its result, so that the binary32 error of z is bounded
-// by the contraction's own magnitude (see kContractErr).
+// the lane pair (n, n+32).  In the draft and residual passes the chain
+// accumulates B from zero and the backbone logits are added to its result, so
+// that the binary32 error of z is bounded by the contraction's own magnitude
+// (see kContractErr); the c* pass, which brackets nothing, seeds the
+// accumulator with them.  The c* and residual passes read U and T with the
+// nontemporal hint (streamed once).  At most 32 rows (bf16) the draft runs
+// k_bias_small instead: 4-wave workgroups on tile-granular splits, each wave
+// streaming its own tiles with no LDS staging.
 // Binary32 rows compute the same bias with a VALU dot product.
 #include "device_common.h"
 #include "draft_epilogue.h"
