@@ -79,7 +79,7 @@ def test_tiny_config(dev):
 
 
 @pytest.mark.parametrize("R,gamma,V", [(32, 4, 5000), (40, 3, 4099), (3, 5, 2049), (1, 1, 40),
-                                       (300, 2, 3000), (64, 2, 33)])
+                                       (300, 2, 3000), (64, 2, 33), (600, 2, 2048), (33, 3, 6000)])
 def test_bf16_shapes(dev, R, gamma, V):
     """bf16 rows on the matrix-core path: ragged vocabularies (not multiples of
     the 32-token tile, and of the 8-element vector load), several row blocks."""
@@ -169,9 +169,13 @@ def test_verify_lengths(dev):
     _run_case(dev, cfg, lengths=lengths, check_schedule=False)
 
 
-def test_fp32_ragged(dev):
+@pytest.mark.parametrize("R,gamma,V", [(7, 3, 1001), (70, 2, 1001), (300, 2, 520)])
+def test_fp32_ragged(dev, R, gamma, V):
+    """Binary32 rows: at most 32 rows (the rank split across the 8 waves), one
+    row block of more than 32 rows, and two row blocks; ragged vocabularies."""
     from draft_sampling_verification_w1_amd import synth
-    cfg = synth.scaled(synth.CONFIGS["tiny"], name="f32_ragged", R=7, gamma=3, V=1001, n_sps=28)
+    cfg = synth.scaled(synth.CONFIGS["tiny"], name=f"f32_{R}x{gamma}x{V}", R=R, gamma=gamma, V=V,
+                       n_sps=R * (gamma + 1))
     _run_case(dev, cfg)
 
 
