@@ -600,6 +600,7 @@ def main():
     avg_s = dom_ms / launches * 1e-3
     n_rows = int(lengths.sum())
     nb = algorithmic_bytes(dom, cfg, n_bonus, n_rows)
+    traffic = measured_traffic(dom)
     achieved = nb / avg_s / 1e9
     path_b = path_bytes(cfg, n_bonus, n_rows)
     log("[bench] per-step kernel time (ms): " +
@@ -626,8 +627,10 @@ def main():
                    "path_hbm_frac": round(path_b / (ms * 1e-3) / (HBM_PEAK_GBS * 1e9), 4)},
         "roofline": {"kernel": dom, "bound": "hbm", "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": measured_traffic(dom), "bytes_per_launch": int(nb),
-                     "avg_launch_us": round(avg_s * 1e6, 2)},
+                     "traffic": traffic, "bytes_per_launch": int(nb),
+                     "avg_launch_us": round(avg_s * 1e6, 2),
+                     # measured bytes (FETCH + WRITE) per launch over the same launch time
+                     "traffic_GBps": None if traffic is None else round(traffic / avg_s / 1e9, 1)},
         "kernels_ms_per_step": {k: round(v[1], 4) for k, v in per_step.items()},
         "profiled_ms_per_step": round(prof_ms, 4),
         "mean_accepted": round(float(n_acc.mean()), 3),
