@@ -301,6 +301,10 @@ __device__ void bias_body(const BiasPassArgs& a, int split, int nsplit, int row_
   const int c_end = (t_end + ST - 1) / ST;
 
   const int row = row0 + wave * 32 + n;
+  // a wave without rows (a partial row block) stages its share of each stage
+  // and meets the barriers but computes nothing: its matrix-core chains would
+  // take the matrix unit from the live wave on the same SIMD
+  const bool wave_live = row0 + wave * 32 < active_rows;
   // the draft's B operands come ready-made from the previous position's select
   // (a.bop), except at the first position
   const bool bop_ready = MODE == kModeDraft && a.bop != nullptr;
@@ -420,7 +424,7 @@ __device__ void bias_body(const BiasPassArgs& a, int split, int nsplit, int row_
       store_stage(d, c);
       load_stage(d, c + D);
       stage_barrier();  // stage c's W2 tiles visible to every wave
-      if (c < c_end) {
+      if (c < c_end && wave_live) {
         const uint8_t* ra_lds = sA[c & 1];
         const uint8_t* ru_lds = &sR[wave][0][n * SEG];
         const uint8_t* rt_lds = &sR[wave][NR - 1][n * SEG];
