@@ -16,7 +16,7 @@ CSRC = os.path.join(PKG, "csrc")
 OBJDIR = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libdspark.so")
 SOURCES = ["bias_pass.hip", "select.hip", "verify_aux.hip", "schedule.hip", "misc.hip", "acceptance.hip",
-           "sts.hip", "api.hip"]
+           "sts.hip", "check.hip", "api.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",

@@ -618,6 +618,24 @@ __attribute__((visibility("default"))) int dspark_confidence(
   return ok();
 }
 
+__attribute__((visibility("default"))) int dspark_check_inputs(
+    const dspark_problem* p, const void* U, const void* T, const void* W1, const void* W2,
+    const int32_t* anchors, const int32_t* tokens, const float* c, int64_t* counts, void* stream) {
+  if (int e = check_problem(p)) return e;
+  if (!counts) return fail(DSPARK_ERR_ARG, "check_inputs: counts must be non-NULL");
+  const uintptr_t esz = p->dtype == DSPARK_BF16 ? 2 : 4;
+  const void* logits[4] = {U, T, W1, W2};
+  for (const void* q : logits)
+    if ((uintptr_t)q % esz)
+      return fail(DSPARK_ERR_ARG, "check_inputs: U, T, W1, W2 must be aligned to %d bytes", (int)esz);
+  if ((uintptr_t)anchors % 4 || (uintptr_t)tokens % 4 || (uintptr_t)c % 4 || (uintptr_t)counts % 8)
+    return fail(DSPARK_ERR_ARG, "check_inputs: misaligned anchors, tokens, c or counts");
+  hipError_t e = launch_check_inputs(p->dtype == DSPARK_BF16, p->R, p->gamma, p->V, U, T, W1, W2,
+                                     anchors, tokens, c, counts, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "check_inputs");
+  return ok();
+}
+
 __attribute__((visibility("default"))) int dspark_schedule(int32_t R, int32_t gamma,
                                                            const float* c, const float* sps,
                                                            int32_t n_sps, float* a,

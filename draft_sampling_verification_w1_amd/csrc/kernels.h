@@ -226,6 +226,13 @@ hipError_t launch_finalize(int R, int gamma, const VerifyWs& w, float* cstar, hi
 // ---- other stages ---------------------------------------------------------
 hipError_t launch_pack_w2(bool bf16, int V, const void* W2, void* W2p, hipStream_t stream);
 hipError_t launch_logpd(int rows, int V, const double* lse, float* zl, hipStream_t stream);
+// Device-side input check: counts (int64, device) of the kCheckCounts classes
+// of dspark_check_inputs, overwritten.
+constexpr int kCheckCounts = 6;
+hipError_t launch_check_inputs(bool bf16, int R, int gamma, int V, const void* U, const void* T,
+                               const void* W1, const void* W2, const int32_t* anchors,
+                               const int32_t* tokens, const float* c, int64_t* counts,
+                               hipStream_t stream);
 hipError_t launch_confidence(bool w1_bf16, int R, int gamma, int V, int H, const uint16_t* h,
                              const float* w, const float* temps, const void* W1,
                              const int32_t* anchors, const int32_t* tokens, float* c,

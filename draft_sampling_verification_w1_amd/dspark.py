@@ -22,7 +22,7 @@ SYMBOLS = ("dspark_w2_packed_bytes", "dspark_pack_w2", "dspark_workspace_bytes",
            "dspark_draft_step", "dspark_draft_step_noalloc", "dspark_verify", "dspark_confidence", "dspark_schedule",
            "dspark_schedule_capacity", "dspark_schedule_topk", "dspark_schedule_threshold",
            "dspark_acceptance_stats", "dspark_sts_workspace_bytes", "dspark_sts_fit",
-           "dspark_last_error", "dspark_timing_enable",
+           "dspark_check_inputs", "dspark_last_error", "dspark_timing_enable",
            "dspark_timing_report")
 
 
@@ -75,6 +75,7 @@ def lib() -> ctypes.CDLL:
         L.dspark_sts_workspace_bytes.restype = ctypes.c_size_t
         L.dspark_sts_fit.argtypes = [ctypes.c_int32, ctypes.c_int32, _vp, _vp, ctypes.c_int32, _vp,
                                      ctypes.c_int32, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
+        L.dspark_check_inputs.argtypes = [P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]
         L.dspark_last_error.restype = ctypes.c_char_p
         L.dspark_timing_enable.argtypes = [ctypes.c_int]
         L.dspark_timing_report.argtypes = [ctypes.c_char_p, ctypes.c_size_t]
@@ -82,6 +83,7 @@ def lib() -> ctypes.CDLL:
                      "dspark_verify", "dspark_confidence",
                      "dspark_schedule", "dspark_schedule_capacity", "dspark_schedule_topk",
                      "dspark_schedule_threshold", "dspark_acceptance_stats", "dspark_sts_fit",
+                     "dspark_check_inputs",
                      "dspark_timing_enable", "dspark_timing_report"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
@@ -268,6 +270,33 @@ def confidence(h, w, temps, W1, anchors, tokens, seed: int = 0, out=None):
     _check(lib().dspark_confidence(ctypes.byref(p), H, _ptr(h), _ptr(w), _ptr(temps), _ptr(W1),
                                    _ptr(anchors), _ptr(tokens), _ptr(c), _stream()))
     return c
+
+
+CHECK_FIELDS = ("anchors", "tokens", "U", "T", "W", "c")
+
+
+def check_inputs(R: int, gamma: int, V: int, dtype, U=None, T=None, W1=None, W2=None,
+                 anchors=None, tokens=None, c=None) -> dict:
+    """Device-side check of the values the host cannot see (dspark_check_inputs):
+    the number of anchors / tokens outside [0, V), of NaN or +inf logits in U
+    and T, of non-finite weights in W1 and W2 (unpacked, [256, V]) and of
+    confidences outside [0, 1].  Any tensor may be None."""
+    given = [t for t in (U, T, W1, W2, anchors, tokens, c) if t is not None]
+    dev = given[0].device if given else torch.device("cuda")
+    for t, name, dt, shape in ((U, "U", dtype, (R, gamma, V)), (T, "T", dtype, (R, gamma + 1, V)),
+                               (W1, "W1", dtype, (V, 256)), (W2, "W2", dtype, (256, V)),
+                               (anchors, "anchors", torch.int32, (R,)),
+                               (tokens, "tokens", torch.int32, (R, gamma)),
+                               (c, "c", torch.float32, (R, gamma))):
+        if t is not None:
+            _need(t, name, dtype=dt, shape=shape)
+    counts = torch.empty(len(CHECK_FIELDS), dtype=torch.int64, device=dev)
+    p = problem(R, gamma, V, dtype, 0)
+    _check(lib().dspark_check_inputs(ctypes.byref(p), _ptr(U), _ptr(T), _ptr(W1), _ptr(W2),
+                                     _ptr(anchors), _ptr(tokens), _ptr(c), _ptr(counts),
+                                     _stream()))
+    vals = counts.cpu().tolist()
+    return dict(zip(CHECK_FIELDS, vals))
 
 
 def schedule(c, sps, with_path: bool = True, out=None):

@@ -260,6 +260,23 @@ int dspark_sts_fit(int32_t N, int32_t gamma, const double* s, const uint8_t* y, 
                    const double* grid, int32_t bins, float* temps, int64_t* ece_units,
                    int64_t* ece1_units, float* a, void* ws, size_t ws_bytes, void* stream);
 
+/* Device-side check of the values the host cannot see, the preconditions
+ * above (a debugging aid, off the hot path: one pass over every tensor given).
+ * counts: int64 [6] in device memory, overwritten with the number of
+ *   0: anchors [R] outside [0, V)
+ *   1: tokens [R, gamma] outside [0, V)
+ *   2: entries of U [R, gamma, V] that are NaN or +inf (-inf masks an entry)
+ *   3: entries of T [R, gamma+1, V] that are NaN or +inf
+ *   4: entries of W1 [V, 256] and W2 [256, V] (as given to dspark_pack_w2)
+ *      that are NaN or infinite
+ *   5: confidences c [R, gamma] (float32) outside [0, 1] or NaN.
+ * Any tensor may be NULL (its count stays 0).  U, T, W1 and W2 are in p->dtype
+ * and must be aligned to their element size, the int32 / float32 tensors to 4
+ * bytes and counts to 8. */
+int dspark_check_inputs(const dspark_problem* p, const void* U, const void* T, const void* W1,
+                        const void* W2, const int32_t* anchors, const int32_t* tokens,
+                        const float* c, int64_t* counts, void* stream);
+
 /* Message for the last failing call on this thread ("" if none). */
 const char* dspark_last_error(void);
 

@@ -144,6 +144,29 @@ def test_sts_validation(L):
     assert lib.dspark_sts_fit(10, 4, fake, fake, 8, fake, 15, fake, fake, fake, fake, fake, need - 1, None) == -4
 
 
+def test_check_inputs_validation(L):
+    """The device-side input check refuses a missing counts buffer and
+    misaligned tensors on the host."""
+    lib = L.lib()
+    fake = ctypes.c_void_p(0x1000)
+    p = _p(L, dtype=1)
+    assert lib.dspark_check_inputs(ctypes.byref(p), fake, None, None, None, None, None, None, None,
+                                   None) == -1
+    assert b"counts" in lib.dspark_last_error()
+    # bf16 tensors need 2-byte alignment, int32 / float32 ones 4, counts 8
+    assert lib.dspark_check_inputs(ctypes.byref(p), ctypes.c_void_p(0x1001), None, None, None, None,
+                                   None, None, fake, None) == -1
+    assert lib.dspark_check_inputs(ctypes.byref(p), None, None, None, None, ctypes.c_void_p(0x1002),
+                                   None, None, fake, None) == -1
+    assert lib.dspark_check_inputs(ctypes.byref(p), None, None, None, None, None, None, None,
+                                   ctypes.c_void_p(0x1004), None) == -1
+    p = _p(L, dtype=0)
+    assert lib.dspark_check_inputs(ctypes.byref(p), ctypes.c_void_p(0x1002), None, None, None, None,
+                                   None, None, fake, None) == -1
+    assert lib.dspark_check_inputs(ctypes.byref(_p(L, R=0)), None, None, None, None, None, None,
+                                   None, fake, None) == -2
+
+
 def test_noalloc_draft_validation(L):
     """The no-allocation draft entry point checks its arguments and its scratch
     size on the host before touching a device."""
