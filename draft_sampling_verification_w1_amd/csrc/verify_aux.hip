@@ -119,11 +119,15 @@ __global__ __launch_bounds__(256) void k_target_lse(int gamma, int V, const E* T
   const int v0 = split * chunk;
   const int v1 = min(V, v0 + chunk);
   const bool vec_ok = w.vec_ok != 0;
-  // Running max m and s = sum exp(x - m).  Each exponent is one fma,
-  // fma(x, L, -m2) with m2 = fl(m L) (L = log2 e): rounded relative to
-  // |x - m| only; the exact residual lo = m L - m2 of the one rounded product
-  // is taken out of every chunk sum as the factor 2^-lo ~ 1 - lo ln 2.
-  float m = -INFINITY, m2 = 0.f, corr = 1.f;
+  // Running max m and s = sum 2^(x L - K) against an integer reference
+  // K = ceil(fl(m L)) (L = log2 e in binary32).  Each exponent is one fma,
+  // fma(x, L, -K), rounded relative to |x L - K| only; a rise of K rescales s
+  // by an exact power of two (the wave meets a new maximum in some lane at
+  // almost every step, so this branch must stay cheap).  At the end s is
+  // brought to sum exp(x - m) by the factor 2^(K - m L), in binary64 with the
+  // same L, so that an element's residual scaling error is |x - m| times the
+  // error of L only.
+  float m = -INFINITY, kf = 0.f;
   double s = 0.0;
   for (int v = v0 + 16 * threadIdx.x; v < v1; v += 16 * 256) {
     float x[16];
@@ -132,20 +136,25 @@ __global__ __launch_bounds__(256) void k_target_lse(int gamma, int V, const E* T
 #pragma unroll
     for (int j = 1; j < 16; ++j) mt = fmaxf(mt, x[j]);
     if (mt > m) {
-      if (m != -INFINITY) s *= exp((double)m - (double)mt);
+      const float kn = ceilf(mt * kLog2e);
+      if (m == -INFINITY) {
+        kf = kn;
+      } else if (kn > kf) {
+        s = ldexp(s, (int)fmax((double)kf - (double)kn, -2000.0));
+        kf = kn;
+      }
       m = mt;
-      m2 = m * kLog2e;
-      corr = fmaf(-fmaf(m, kLog2e, -m2), kLn2, 1.f);
     }
     if (m != -INFINITY) {
       float e[16];
 #pragma unroll
-      for (int j = 0; j < 16; ++j) e[j] = __builtin_amdgcn_exp2f(fmaf(x[j], kLog2e, -m2));
+      for (int j = 0; j < 16; ++j) e[j] = __builtin_amdgcn_exp2f(fmaf(x[j], kLog2e, -kf));
       const float a0 = ((e[0] + e[1]) + (e[2] + e[3])) + ((e[4] + e[5]) + (e[6] + e[7]));
       const float a1 = ((e[8] + e[9]) + (e[10] + e[11])) + ((e[12] + e[13]) + (e[14] + e[15]));
-      s += (double)((a0 + a1) * corr);
+      s += (double)(a0 + a1);
     }
   }
+  if (m != -INFINITY) s *= exp2((double)kf - (double)m * (double)kLog2e);
   block_lse(m, s);
   if (threadIdx.x == 0) {
     const int64_t o = (int64_t)i * w.ns_t + split;  // ns_t: the record stride
