@@ -61,6 +61,9 @@ struct DraftLane {
 // once per block: log sum_v e^(z_v) = mt + (log2 s - mt2_lo) ln 2, and the
 // block sum enters the running sum as s 2^(-mt2_lo).  What remains is the
 // hardware exp2 / log2 error and the 32-term sum (a few 2^-24 relative).
+// (One fma on z = fl(u + b) instead saves 16 instructions per block but
+// rounds relative to |z|: the lse error at |lse| ~ 20 grows from ~1.5e-7 to
+// ~7e-7, most of the 1e-6 margin of the acceptance decisions.)
 __device__ __forceinline__ void draft_block_epilogue(DraftLane& st, const float* u, const float* b,
                                                      int r, int k, int t, bool first, uint64_t seed,
                                                      float dz) {
@@ -78,11 +81,13 @@ __device__ __forceinline__ void draft_block_epilogue(DraftLane& st, const float*
     e[j] = __builtin_amdgcn_exp2f(fmaf(b[j], kLog2e, fmaf(u[j], kLog2e, -mt2)));
   const float s = sum_halves(sum16(e));
   const float sn = fmaf(s, -mt2_lo * kLn2, s);  // s 2^(-mt2_lo) to first order (|mt2_lo| < 2^-17)
-  if (mt > st.M) {
-    st.S = st.S * (double)__builtin_amdgcn_exp2f((st.M - mt) * kLog2e) + (double)sn;
-    st.M = mt;
-  } else {
-    st.S += (double)(sn * __builtin_amdgcn_exp2f((mt - st.M) * kLog2e));
+  {
+    // one exponential whichever maximum is larger (lanes of a wave differ),
+    // the smaller against the larger; st.M = -inf at the first block gives 0
+    const bool up = mt > st.M;
+    const float f = __builtin_amdgcn_exp2f(-fabsf(st.M - mt) * kLog2e);
+    st.S = up ? fma(st.S, (double)f, (double)sn) : fma((double)sn, (double)f, st.S);
+    st.M = up ? mt : st.M;
   }
   const float sc = fmaf(__builtin_amdgcn_logf(s) - mt2_lo, kLn2, mt) +
                    gumbel_f32(word_of(st.words, t & 3));
