@@ -19,6 +19,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -83,17 +84,38 @@ def path_bytes(cfg, n_bonus, n_rows=None):
     return draft + verify + head + outputs
 
 
+def source_digest(path):
+    """SHA-256 over a kernel source and, in the order first met, every local
+    header it includes (#include "..." found beside it), so that a change to
+    any code compiled into the kernel changes the digest."""
+    h = hashlib.sha256()
+    seen, todo = set(), [os.path.normpath(path)]
+    while todo:
+        p = todo.pop(0)
+        if p in seen:
+            continue
+        seen.add(p)
+        with open(os.path.join(HERE, p), "rb") as f:
+            data = f.read()
+        h.update(p.encode() + b"\0" + data)
+        for inc in re.findall(rb'^\s*#include\s+"([^"]+)"', data, flags=re.M):
+            q = os.path.normpath(os.path.join(os.path.dirname(p), inc.decode()))
+            if os.path.exists(os.path.join(HERE, q)):
+                todo.append(q)
+    return h.hexdigest()
+
+
 def measured_traffic(kernel):
     """HBM bytes per launch of `kernel` from the committed counter summary
     (FETCH_SIZE + WRITE_SIZE, scaled by a plain copy's reading), or None when
-    there is none or the kernel's source changed since it was taken."""
+    there is none or the kernel's code (its source or a local header it
+    includes) changed since it was taken."""
     try:
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
         ent = t["kernels"][kernel]
-        with open(os.path.join(HERE, ent["source"]), "rb") as f:
-            if hashlib.sha256(f.read()).hexdigest() != ent["source_sha256"]:
-                return None
+        if source_digest(ent["source"]) != ent["sources_sha256"]:
+            return None
         return ent["bytes_per_launch"]
     except (OSError, KeyError, ValueError):
         return None
@@ -119,8 +141,8 @@ def write_traffic(fetch_csv, write_csv, copy_mib, commands):
     """profiles/traffic.json from two rocprofv3 --pmc runs (FETCH_SIZE, then
     WRITE_SIZE, KiB per dispatch) of `bench.py --calibrate-copy copy_mib`: each
     counter is scaled by what it reads for the three plain copies of copy_mib
-    MiB, and each kernel keyed by the hash of its source (stale once the
-    source changes).  Prints the per-kernel table."""
+    MiB, and each kernel keyed by the digest of its source and local headers
+    (stale once any of them changes).  Prints the per-kernel table."""
     import csv
     pkg = "draft_sampling_verification_w1_amd"
 
@@ -152,9 +174,7 @@ def write_traffic(fetch_csv, write_csv, copy_mib, commands):
         rd = sum(fv) / len(fv) * 1024 * fetch_scale
         wr = sum(wv) / len(wv) * 1024 * write_scale
         path = f"{pkg}/{src}"
-        with open(os.path.join(HERE, path), "rb") as f:
-            sha = hashlib.sha256(f.read()).hexdigest()
-        out["kernels"][name] = {"source": path, "source_sha256": sha,
+        out["kernels"][name] = {"source": path, "sources_sha256": source_digest(path),
                                 "bytes_per_launch": int(rd + wr), "read_bytes": int(rd),
                                 "write_bytes": int(wr)}
         print(f"| {name} (`{pat}`) | {len(fv)} | {sum(fv) / len(fv):.1f} | {sum(wv) / len(wv):.1f} | "

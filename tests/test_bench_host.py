@@ -36,10 +36,29 @@ def test_write_traffic_scales_by_the_copy(tmp_path, monkeypatch):
     k = t["kernels"]["draft_bias"]
     assert k["read_bytes"] == int(1100.0 * 1024 * 2.0)
     assert k["write_bytes"] == int(20.0 * 1024)
-    assert k["source"].endswith("csrc/bias_pass.hip") and len(k["source_sha256"]) == 64
+    assert k["source"].endswith("csrc/bias_pass.hip") and len(k["sources_sha256"]) == 64
     assert "cstar_bias" not in t["kernels"]  # no counter rows, no entry
     # the bench reads it back while the source is unchanged
     assert bench.measured_traffic("draft_bias") == k["bytes_per_launch"]
+
+
+def test_traffic_goes_stale_when_an_included_header_changes(tmp_path, monkeypatch):
+    # a kernel source that includes a local header: the digest covers both
+    src = tmp_path / "pkg" / "csrc"
+    src.mkdir(parents=True)
+    (src / "k.hip").write_text('#include "h.h"\n#include <hip/hip_runtime.h>\nint k;\n')
+    (src / "h.h").write_text("int h = 1;\n")
+    monkeypatch.setattr(bench, "HERE", str(tmp_path))
+    d0 = bench.source_digest("pkg/csrc/k.hip")
+    assert d0 == bench.source_digest("pkg/csrc/k.hip")
+    out = tmp_path / "traffic.json"
+    out.write_text(json.dumps({"kernels": {"draft_bias": {
+        "source": "pkg/csrc/k.hip", "sources_sha256": d0, "bytes_per_launch": 123}}}))
+    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(out))
+    assert bench.measured_traffic("draft_bias") == 123
+    (src / "h.h").write_text("int h = 2;\n")  # only the header changes
+    assert bench.source_digest("pkg/csrc/k.hip") != d0
+    assert bench.measured_traffic("draft_bias") is None
 
 
 def test_write_traffic_calibrates_on_the_first_three_copies(tmp_path, monkeypatch):
