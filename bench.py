@@ -491,7 +491,7 @@ def main():
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               "(the hot path shards over requests with no exchange except one all-gather "
-              "for the scheduler, which this build does not run).", file=sys.stderr)
+              "for the scheduler; the library runs on one GPU).", file=sys.stderr)
         sys.exit(2)
 
     import torch
