@@ -169,6 +169,37 @@ def test_verify_lengths(dev):
     _run_case(dev, cfg, lengths=lengths, check_schedule=False)
 
 
+def _random_problem(i):
+    """Problem i of the seeded sweep: shape, dtype, logit and weight scales,
+    target rule, SPS curve and a 64-bit draw seed with high bits set; every
+    third problem verifies per-request lengths instead of all positions."""
+    from draft_sampling_verification_w1_amd import synth
+    rng = np.random.default_rng(9000 + i)
+    bf16 = bool(rng.integers(0, 4))  # three in four on the matrix-core path
+    R = int(rng.integers(1, 81)) if rng.integers(0, 4) else int(rng.integers(81, 301))
+    gamma = int(rng.integers(1, 7))
+    V = int(rng.choice([int(rng.integers(1, 97)), int(rng.integers(97, 6001))]))
+    base = synth.CONFIGS["qwen3_4b" if bf16 else "tiny"]
+    cfg = synth.scaled(base, name=f"sweep{i}", R=R, gamma=gamma, V=V,
+                       seed=int(rng.integers(1 << 62, 1 << 63)) | (int(rng.integers(0, 2)) << 63),
+                       u_sigma=float(rng.choice([1.0, 3.0, 6.0])),
+                       w_sigma=float(rng.choice([0.01, 0.05, 0.3])),
+                       zipf_boost=float(rng.choice([0.0, 8.0])),
+                       target_from_draft=bool(rng.integers(0, 2)),
+                       noise=str(rng.choice(["unit", "rising", "decaying"])),
+                       sps=str(rng.choice(["tiny", "knee2R"])), n_sps=R * (gamma + 1))
+    lengths = rng.integers(0, gamma + 1, R).astype(np.int32) if i % 3 == 2 else None
+    return cfg, lengths
+
+
+@pytest.mark.parametrize("i", range(40))
+def test_random_problems(dev, i):
+    """A seeded sweep of small problems through draft (tokens, lse, log q and
+    every log p^d), verify and the scheduler against the oracle."""
+    cfg, lengths = _random_problem(i)
+    _run_case(dev, cfg, lengths=lengths, check_schedule=lengths is None)
+
+
 @pytest.mark.parametrize("R,gamma,V", [(7, 3, 1001), (70, 2, 1001), (300, 2, 520)])
 def test_fp32_ragged(dev, R, gamma, V):
     """Binary32 rows: at most 32 rows (the rank split across the 8 waves), one
