@@ -152,3 +152,77 @@ def test_full_size_large_vocab(dev):
 
 def test_full_size_scheduled_round(dev):
     _full_round(dev, "full_round", with_confidence=True)
+
+
+def test_maximum_batch(dev):
+    """The library's batch limits, R = 65,536 requests and R * gamma = 2^20
+    positions, at a two-tile vocabulary (V = 40): draft and verify of the
+    whole batch against the oracle, compared with array operations (the
+    scheduler's own limit, R * gamma <= 16,384, is covered above)."""
+    import time
+    import torch
+    from oracle import oracle as O
+    from draft_sampling_verification_w1_amd import synth
+    from parity_util import RTOL, ATOL, TIE, STATS
+    cfg = synth.scaled(synth.CONFIGS["high_concurrency"], name="max_batch", R=65536, gamma=16, V=40,
+                       n_sps=65536 * 17)
+    R, g, V = cfg.R, cfg.gamma, cfg.V
+    t0 = time.time()
+    W1, W2 = synth.weights(cfg)
+    U, Ub = synth.backbone(cfg)
+    A = synth.anchors(cfg)
+    log(f"maximum batch: R={R} gamma={g} V={V}; inputs in {time.time() - t0:.1f}s")
+
+    dU, dW1, dA = to_dev(U), to_dev(W1), to_dev(A)
+    W2p = dev.pack_w2(to_dev(W2), V)
+    tok, lse, logq = dev.draft_step(dU, dW1, W2p, dA, cfg.seed)
+    torch.cuda.synchronize()
+    tok_h, lse_h, logq_h = tok.cpu().numpy(), lse.cpu().numpy(), logq.cpu().numpy()
+    od = O.draft(U, W1, W2, A, cfg.seed)
+    # a request is compared up to its first differing token, which must be
+    # an oracle near-tie (the later positions then condition on other tokens)
+    diff = tok_h != od["tokens"]
+    first = np.where(diff.any(axis=1), diff.argmax(axis=1), g)
+    tied = np.nonzero(first < g)[0]
+    assert np.all(od["margin"][tied, first[tied]] < TIE), "draft token mismatch beyond a near-tie"
+    upto = np.arange(g)[None, :] < first[:, None]
+    np.testing.assert_allclose(lse_h[upto], od["lse"][upto], rtol=RTOL, atol=ATOL)
+    np.testing.assert_allclose(logq_h[upto], od["logq"][upto], rtol=0, atol=RTOL)
+    draws = int(upto.sum()) + tied.size
+    STATS["draws"] += draws
+    STATS["ties"] += tied.size
+    assert tied.size <= 1e-4 * draws
+    log(f"  draft: {draws} positions compared, {tied.size} near-ties")
+
+    # targets from the oracle's draft logits (the workload's recipe)
+    W2f = O.to_f64(W2)
+    base = np.empty((R, g, V), np.float32)
+    for k in range(1, g + 1):
+        prev = A if k == 1 else od["tokens"][:, k - 2]
+        base[:, k - 1, :] = O.draft_logits(U[:, k - 1, :], W1, W2f, prev)
+    T = np.empty((R, g + 1, V), np.uint16)
+    for r in range(R):
+        T[r] = synth.target_rows(cfg, r, base[r], Ub[r])
+    gv = dev.verify(dU, dW1, W2p, dA, tok, lse, logq, to_dev(T), None, cfg.seed)
+    torch.cuda.synchronize()
+    gn = {k: (v.cpu().numpy() if v is not None else None) for k, v in gv.items()}
+    req = np.nonzero(first == g)[0].astype(np.int32)
+    ov = O.verify(U, W1, W2, A, tok_h, T, None, cfg.seed, requests=req, chunk=4096)
+    np.testing.assert_allclose(gn["cstar"][req], ov["cstar"], rtol=RTOL, atol=ATOL)
+    np.testing.assert_allclose(gn["lse_t"][req], ov["lse_t"], rtol=RTOL, atol=ATOL)
+    # acceptance: a differing decision must be an oracle near-tie
+    am = gn["accept_mask"][req] != ov["accept_mask"]
+    mism = np.nonzero(am.any(axis=1))[0]
+    k0 = am.argmax(axis=1)
+    assert np.all(ov["acc_margin"][mism, k0[mism]] < TIE), "accept decision differs beyond a near-tie"
+    same = np.ones(req.size, bool)
+    same[mism] = False
+    assert np.array_equal(gn["n_accept"][req][same], ov["n_accept"][same])
+    tok_diff = np.nonzero(same & (gn["out_token"][req] != ov["out_token"]))[0]
+    assert np.all(ov["out_margin"][tok_diff] < TIE), "corrective / bonus token differs beyond a near-tie"
+    ties = mism.size + tok_diff.size
+    STATS["draws"] += req.size
+    STATS["ties"] += ties
+    assert ties <= 1e-4 * req.size * g
+    log(f"  verify: {req.size} requests compared, {ties} near-ties; mean accepted "
+        f"{ov['n_accept'].mean():.3f}")
