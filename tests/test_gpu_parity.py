@@ -370,6 +370,16 @@ def test_single_token_vocabulary(dev):
     _run_case(dev, cfg)
 
 
+def test_million_token_vocabulary(dev):
+    """V = 1,000,003 (about 2^20, ragged; W1 and W2 512 MB each in bf16): the
+    small-batch draft with 256 splits of ~122 tiles, the c* and target-lse
+    passes with hundreds of splits per row, and the binary64 draws over 31,251
+    blocks, against the oracle."""
+    from draft_sampling_verification_w1_amd import synth
+    cfg = synth.scaled(synth.CONFIGS["qwen3_4b"], name="v1m", R=2, gamma=2, V=1_000_003, n_sps=2 * 3)
+    _run_case(dev, cfg)
+
+
 def test_largest_block(dev):
     """gamma = 64, the largest block the library accepts."""
     from draft_sampling_verification_w1_amd import synth
