@@ -89,7 +89,7 @@ struct DraftLayout {
 
 DraftLayout draft_layout(const dspark_problem* p) {
   DraftLayout L;
-  L.g = bias_geometry(kModeDraft, p->R, p->V);
+  L.g = bias_geometry(kModeDraft, p->dtype == DSPARK_BF16, p->R, p->V);
   // the small-batch pass (at most 32 rows, bf16) may use more, tile-granular splits
   const int ns_small = p->dtype == DSPARK_BF16 ? small_draft_splits(p->R, p->V) : 0;
   const size_t n = (size_t)p->R * (ns_small > L.g.nsplit ? ns_small : L.g.nsplit);
@@ -122,8 +122,8 @@ struct VerifyLayout {
 VerifyLayout verify_layout(const dspark_problem* p) {
   VerifyLayout L;
   const size_t R = p->R, rows = (size_t)p->R * p->gamma;
-  L.gc = bias_geometry(kModeCstar, (int)rows, p->V);
-  L.gr = bias_geometry(kModeResidual, p->R, p->V);
+  L.gc = bias_geometry(kModeCstar, p->dtype == DSPARK_BF16, (int)rows, p->V);
+  L.gr = bias_geometry(kModeResidual, p->dtype == DSPARK_BF16, p->R, p->V);
   // the c* pass spreads its workgroups over the row blocks that hold verified
   // rows (known on the device only): up to one split per workgroup
   L.grid_c = L.gc.nsplit * L.gc.row_blocks;

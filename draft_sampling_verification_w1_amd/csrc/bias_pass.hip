@@ -785,13 +785,14 @@ __global__ __launch_bounds__(256) void k_bias_small(const BiasPassArgs a) {
 }  // namespace
 
 // Vocabulary splits: enough workgroups for one full round on MI355X (256 CUs,
-// one 8-wave workgroup each), never more splits than pipeline stages (2 tiles).
-BiasGeometry bias_geometry(int mode, int nrows, int V) {
+// one 8-wave workgroup each), never more splits than pipeline stages (2 tiles
+// in the bf16 passes; the binary32 pass works tile by tile).
+BiasGeometry bias_geometry(int mode, bool bf16, int nrows, int V) {
   constexpr int kSlots = 256;
   BiasGeometry g;
   g.rows_per_block = kRowsPerBlock;
   g.row_blocks = (nrows + kRowsPerBlock - 1) / kRowsPerBlock;
-  g.tiles_per_stage = 2;
+  g.tiles_per_stage = bf16 ? 2 : 1;
   const int ntiles = (V + kTile - 1) / kTile;
   const int nstages = (ntiles + g.tiles_per_stage - 1) / g.tiles_per_stage;
   g.nsplit = min(nstages, max(1, (kSlots + g.row_blocks - 1) / g.row_blocks));

@@ -106,7 +106,7 @@ struct BiasGeometry {
   int tiles_per_stage;
   int nsplit;
 };
-BiasGeometry bias_geometry(int mode, int nrows, int V);
+BiasGeometry bias_geometry(int mode, bool bf16, int nrows, int V);
 // Draft splits of the small-batch pass (at most 32 rows, bf16; tile-granular
 // splits, one per workgroup), or 0 when the batch is larger.
 int small_draft_splits(int nrows, int V);
