@@ -274,7 +274,13 @@ static void launch_mode(int R, int gamma, const float* c, const float* sps, floa
                         int32_t* lengths, double* stats, double* theta_path, int32_t* k_io,
                         hipStream_t stream) {
   const int64_t n = (int64_t)R * gamma;
-  if (n <= 4 * kThreads)
+  if (n <= kThreads)
+    hipLaunchKernelGGL((k_schedule<1, MODE>), dim3(1), dim3(kThreads), 0, stream, R, gamma, c,
+                       sps, a, lengths, stats, theta_path, k_io);
+  else if (n <= 2 * kThreads)
+    hipLaunchKernelGGL((k_schedule<2, MODE>), dim3(1), dim3(kThreads), 0, stream, R, gamma, c,
+                       sps, a, lengths, stats, theta_path, k_io);
+  else if (n <= 4 * kThreads)
     hipLaunchKernelGGL((k_schedule<4, MODE>), dim3(1), dim3(kThreads), 0, stream, R, gamma, c,
                        sps, a, lengths, stats, theta_path, k_io);
   else if (n <= 8 * kThreads)

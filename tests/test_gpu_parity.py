@@ -279,7 +279,8 @@ def test_confidence_head(dev, H, dtype):
     np.testing.assert_allclose(gc, oc, rtol=1e-6, atol=0)
 
 
-@pytest.mark.parametrize("R,gamma", [(1, 1), (4, 8), (37, 5), (512, 16), (1024, 16)])
+@pytest.mark.parametrize("R,gamma", [(1, 1), (4, 8), (37, 5), (64, 16), (100, 13), (128, 16), (512, 16),
+                                     (1024, 16)])
 def test_schedule_against_oracle(dev, R, gamma):
     import torch
     from oracle import oracle as O
@@ -299,7 +300,7 @@ def test_schedule_against_oracle(dev, R, gamma):
         compare_schedule(os_, gs["a"].cpu().numpy(), {k: v.cpu().numpy() for k, v in gs.items() if k != "a"})
 
 
-@pytest.mark.parametrize("R,gamma", [(37, 5), (256, 16), (512, 16), (1024, 16)])
+@pytest.mark.parametrize("R,gamma", [(37, 5), (128, 16), (256, 16), (512, 16), (1024, 16)])
 def test_schedule_ties(dev, R, gamma):
     """Factors from {1/4, 1/2, 3/4, 1}: many survival products are equal, across
     requests and within one, so the (r, j) order of equal keys decides which

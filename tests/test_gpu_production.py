@@ -38,7 +38,7 @@ def _confidences(rng, R, gamma, kind):
     return rng.uniform(0.3, 1.0, (R, gamma)).astype(np.float32)
 
 
-@pytest.mark.parametrize("R,gamma", [(1, 1), (37, 5), (256, 16), (512, 16), (1024, 16)])
+@pytest.mark.parametrize("R,gamma", [(1, 1), (37, 5), (100, 13), (256, 16), (512, 16), (1024, 16)])
 @pytest.mark.parametrize("kind", ["uniform", "ties"])
 def test_capacity_and_topk(dev, R, gamma, kind):
     import torch
