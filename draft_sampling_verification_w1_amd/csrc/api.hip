@@ -91,7 +91,7 @@ DraftLayout draft_layout(const dspark_problem* p) {
   DraftLayout L;
   L.g = bias_geometry(kModeDraft, p->dtype == DSPARK_BF16, p->R, p->V);
   // the small-batch pass (at most 32 rows, bf16) may use more, tile-granular splits
-  const int ns_small = p->dtype == DSPARK_BF16 ? small_draft_splits(p->R, p->V) : 0;
+  const int ns_small = p->dtype == DSPARK_BF16 ? small_pass_splits(p->R, p->V) : 0;
   const size_t n = (size_t)p->R * (ns_small > L.g.nsplit ? ns_small : L.g.nsplit);
   Carver c;
   L.pm = c.take(n * sizeof(float));
@@ -112,6 +112,7 @@ int bonus_splits(int R, int V) {
 
 struct VerifyLayout {
   BiasGeometry gc, gr;
+  int ns_r, small_r;  // residual pass: splits (records per row); 1 = the small-batch pass
   int grid_c, rec_c;  // c* pass: workgroups launched, records per row
   int grid_t, ns_t, ns_b;  // target lse: workgroups launched, records per row
   size_t row_ids, counts, req_off, req_len, req_slot, req_mode, resid_ids, bonus_ids;
@@ -124,6 +125,11 @@ VerifyLayout verify_layout(const dspark_problem* p) {
   const size_t R = p->R, rows = (size_t)p->R * p->gamma;
   L.gc = bias_geometry(kModeCstar, p->dtype == DSPARK_BF16, (int)rows, p->V);
   L.gr = bias_geometry(kModeResidual, p->dtype == DSPARK_BF16, p->R, p->V);
+  // at most 32 requests (bf16): the residual rows go through the small-batch
+  // pass, on its tile-granular splits
+  const int ns_small = p->dtype == DSPARK_BF16 ? small_pass_splits(p->R, p->V) : 0;
+  L.small_r = ns_small > 0 ? 1 : 0;
+  L.ns_r = ns_small > 0 ? ns_small : L.gr.nsplit;
   // the c* pass spreads its workgroups over the row blocks that hold verified
   // rows (known on the device only): up to one split per workgroup
   L.grid_c = L.gc.nsplit * L.gc.row_blocks;
@@ -148,9 +154,9 @@ VerifyLayout verify_layout(const dspark_problem* p) {
   L.lt_s = c.take(rows * L.ns_t * sizeof(double));
   L.lse_t = c.take(R * (p->gamma + 1) * sizeof(double));
   L.c_s = c.take(rows * L.rec_c * sizeof(double));
-  L.r_cand = take_cands(c, R * L.gr.nsplit);
-  L.r_candf = take_cands(c, R * L.gr.nsplit);
-  L.r_wpos = c.take(R * L.gr.nsplit * sizeof(float));
+  L.r_cand = take_cands(c, R * L.ns_r);
+  L.r_candf = take_cands(c, R * L.ns_r);
+  L.r_wpos = c.take(R * L.ns_r * sizeof(float));
   L.b_cand = take_cands(c, R * L.ns_b);
   L.bytes = c.off;
   return L;
@@ -330,7 +336,7 @@ int draft_launch(const dspark_problem* p, const void* U, const void* W1, const v
   a.vec_ok = rows_vec_ok(p, U, nullptr);
   a.tiles_per_stage = L.g.tiles_per_stage;
   a.nsplit = L.g.nsplit;
-  if (const int ns = bf16 ? small_draft_splits(p->R, p->V) : 0) {
+  if (const int ns = bf16 ? small_pass_splits(p->R, p->V) : 0) {
     // at most 32 rows: the small-batch pass, tile-granular splits
     a.tiles_per_stage = 1;
     a.nsplit = ns;
@@ -513,7 +519,7 @@ __attribute__((visibility("default"))) int dspark_verify(
   w.ns_t = L.ns_t;
   w.ns_c = L.rec_c;
   w.grid_c = L.grid_c;
-  w.ns_r = L.gr.nsplit;
+  w.ns_r = L.ns_r;
   w.ns_b = L.ns_b;
   w.grid_t = L.grid_t;
   w.vec_ok = rows_vec_ok(p, nullptr, T);
@@ -556,9 +562,9 @@ __attribute__((visibility("default"))) int dspark_verify(
   a.row_ids = w.resid_ids;
   a.row_count = w.counts + 1;
   a.nrows = p->R;
-  a.tiles_per_stage = L.gr.tiles_per_stage;
-  a.nsplit = L.gr.nsplit;
-  a.rec_stride = L.gr.nsplit;
+  a.tiles_per_stage = L.small_r ? 1 : L.gr.tiles_per_stage;
+  a.nsplit = L.ns_r;
+  a.rec_stride = L.ns_r;
   a.dyn = 0;
   a.ps = nullptr;
   a.cand = w.r_cand;
@@ -586,8 +592,8 @@ __attribute__((visibility("default"))) int dspark_verify(
   q.out_tokens = out_token;
   q.row_ids = w.resid_ids;
   q.row_count = w.counts + 1;
-  q.nsplit = L.gr.nsplit;
-  q.tiles_per_stage = L.gr.tiles_per_stage;
+  q.nsplit = L.ns_r;
+  q.tiles_per_stage = L.small_r ? 1 : L.gr.tiles_per_stage;
   q.cand = w.r_cand;
   q.cand_f = w.r_candf;
   q.wpos = w.r_wpos;

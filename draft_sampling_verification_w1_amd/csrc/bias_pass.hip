@@ -657,29 +657,35 @@ __global__ __launch_bounds__(kThreads) void k_bias_f32(const BiasPassArgs a) {
   finish<MODE>(st, rc, row, split, a, h == 0);
 }
 
-// Draft pass for at most 32 rows (one 32-row group, bf16): with a single row
-// group nothing is worth sharing between waves, so every wave streams its own
-// contiguous quarter of the workgroup's tiles with no LDS staging and no
-// barrier: the A operands (packed W2 tile) and the lane's 16 backbone logits
-// are loaded straight into registers, one tile ahead, and each W2 tile crosses
-// the fabric once per position.  Workgroup = split (tile-granular); the four
-// waves' states of each row are merged through LDS at the end.
-template <bool VEC, bool ZOUT>
+// Draft and residual passes for at most 32 rows (one 32-row group, bf16):
+// with a single row group nothing is worth sharing between waves, so every
+// wave streams its own contiguous quarter of the workgroup's tiles with no LDS
+// staging and no barrier: the A operands (packed W2 tile) and the lane's 16
+// backbone logits (and target logits) are loaded straight into registers, one
+// tile ahead, and each W2 tile crosses the fabric once per launch.  Workgroup
+// = split (tile-granular); the four waves' states of each row are merged
+// through LDS at the end.
+template <int MODE, bool VEC, bool ZOUT>
 __global__ __launch_bounds__(256) void k_bias_small(const BiasPassArgs a) {
   constexpr int kW = 4;
+  constexpr bool kNeedT = MODE != kModeDraft;
+  static_assert(MODE == kModeDraft || MODE == kModeResidual, "draft or residual");
+  static_assert(!ZOUT || MODE == kModeDraft, "logits out in the draft only");
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n = lane & 31;
   const int h = lane >> 5;
+  const int active_rows = a.row_count ? min(*a.row_count, a.nrows) : a.nrows;
+  if (active_rows <= 0) return;
   const int split = blockIdx.x;
   const int t0 = split_tile(split, a.nsplit, a.ntiles, 1);
   const int t1 = split_tile(split + 1, a.nsplit, a.ntiles, 1);
   const int per = (t1 - t0 + kW - 1) / kW;
   const int tb = min(t1, t0 + wave * per);
   const int te = min(t1, tb + per);
-  const bool bop_ready = a.bop != nullptr;
-  const RowCtx rc = row_ctx(a, n, a.nrows, true, a.k, !bop_ready);
-  LaneState<kModeDraft> st;
+  const bool bop_ready = MODE == kModeDraft && a.bop != nullptr;
+  const RowCtx rc = row_ctx(a, n, active_rows, true, a.k, !bop_ready);
+  LaneState<MODE> st;
   st.init();
 
   bf16x8 bop[kSteps];
@@ -707,40 +713,57 @@ __global__ __launch_bounds__(256) void k_bias_small(const BiasPassArgs a) {
   const float* tmax = w2_tile_absmax(a.W2p, true, a.ntiles);
   const u32x4* W2q = reinterpret_cast<const u32x4*>(a.W2p);
   const uint16_t* urow = rc.active ? reinterpret_cast<const uint16_t*>(rc.urow) : nullptr;
+  const uint16_t* trow = (kNeedT && rc.active) ? reinterpret_cast<const uint16_t*>(rc.trow) : nullptr;
   float* zrow = nullptr;
   if constexpr (ZOUT)
     if (rc.active) zrow = a.zout + ((int64_t)rc.r * a.gamma + (rc.k - 1)) * (int64_t)a.V;
 
-  // tile loads: 16 A fragments and the lane's 16 logits (tiles past the
-  // wave's range repeat its last tile and are never used)
-  auto load_tile = [&](int t, u32x4* A, u32x4& ulo, u32x4& uhi) {
-    const int tt = min(t, max(te - 1, tb));
-#pragma unroll
-    for (int s = 0; s < kSteps; ++s) A[s] = gload16(W2q + (int64_t)tt * 1024 + s * 64 + lane);
-    const int v = tt * kTile + 16 * h;
-    if (VEC && urow != nullptr && v + 16 <= a.V) {
-      ulo = gload16(urow + v);
-      uhi = gload16(urow + v + 8);
+  // the lane's 16 logits [v, v + 16) of a row (-inf beyond V and for a null row)
+  auto row16 = [&](const uint16_t* row, int v, u32x4& lo, u32x4& hi) {
+    if (VEC && row != nullptr && v + 16 <= a.V) {
+      if constexpr (kNeedT) {
+        lo = gload16_nt(row + v);
+        hi = gload16_nt(row + v + 8);
+      } else {
+        lo = gload16(row + v);
+        hi = gload16(row + v + 8);
+      }
     } else {
-      ulo = chunk_load(urow, v, a.V);
-      uhi = chunk_load(urow, v + 8, a.V);
+      lo = chunk_load(row, v, a.V);
+      hi = chunk_load(row, v + 8, a.V);
     }
   };
-  u32x4 A[kSteps], ulo, uhi;
-  if (tb < te) load_tile(tb, A, ulo, uhi);
+  // tile loads: 16 A fragments and the lane's logits (tiles past the wave's
+  // range repeat its last tile and are never used)
+  struct Tile {
+    u32x4 A[kSteps];
+    u32x4 ulo, uhi, tlo, thi;
+  };
+  auto load_tile = [&](int t, Tile& x) {
+    const int tt = min(t, max(te - 1, tb));
+#pragma unroll
+    for (int s = 0; s < kSteps; ++s) x.A[s] = gload16(W2q + (int64_t)tt * 1024 + s * 64 + lane);
+    const int v = tt * kTile + 16 * h;
+    row16(urow, v, x.ulo, x.uhi);
+    if constexpr (kNeedT) row16(trow, v, x.tlo, x.thi);
+  };
+  Tile cur;
+  if (tb < te) load_tile(tb, cur);
   for (int t = tb; t < te; ++t) {
-    u32x4 An[kSteps], nlo, nhi;
-    load_tile(t + 1, An, nlo, nhi);  // one tile ahead
+    Tile nxt;
+    load_tile(t + 1, nxt);  // one tile ahead
     f32x16 acc;
 #pragma unroll
     for (int j = 0; j < 16; ++j) acc[j] = 0.f;
 #pragma unroll
     for (int s = 0; s < kSteps; ++s)
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(A[s]), bop[s], acc, 0, 0, 0);
-    float z[16], zu[16];
-    decode16(ulo, uhi, zu);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(cur.A[s]), bop[s], acc, 0, 0, 0);
+    float z[16], zu[16], tv[16];
+    decode16(cur.ulo, cur.uhi, zu);
+    // the draft passes the bias and the backbone logits apart, the residual z
 #pragma unroll
-    for (int j = 0; j < 16; ++j) z[j] = acc[j];
+    for (int j = 0; j < 16; ++j) z[j] = (MODE == kModeDraft) ? acc[j] : zu[j] + acc[j];
+    if constexpr (kNeedT) decode16(cur.tlo, cur.thi, tv);
     if constexpr (ZOUT) {
       const int vb = t * kTile + 16 * h;
       if (zrow)
@@ -748,37 +771,53 @@ __global__ __launch_bounds__(256) void k_bias_small(const BiasPassArgs a) {
         for (int j = 0; j < 16; ++j)
           if (vb + j < a.V) zrow[vb + j] = zu[j] + z[j];
     }
-    draft_block_epilogue(st, zu, z, rc.r, rc.k, t, t == tb, a.seed, kz * tile_absmax(tmax, t));
-#pragma unroll
-    for (int s = 0; s < kSteps; ++s) A[s] = An[s];
-    ulo = nlo;
-    uhi = nhi;
+    epilogue<MODE>(st, z, tv, rc, t, t == tb, a.seed, kz * tile_absmax(tmax, t), zu);
+    cur = nxt;
   }
 
   // merge the four waves' states of each row (disjoint tile ranges)
-  __shared__ float sm[kW][32], slo[kW][32], shi1[kW][32], shi2[kW][32];
-  __shared__ double ss[kW][32];
-  __shared__ int sb1[kW][32];
-  if (h == 0) {
-    sm[wave][n] = st.M;
-    ss[wave][n] = st.S;
-    slo[wave][n] = st.cand.lo;
-    shi1[wave][n] = st.cand.hi1;
-    shi2[wave][n] = st.cand.hi2;
-    sb1[wave][n] = st.cand.b1;
-  }
-  __syncthreads();
-  if (wave == 0) {
-    for (int w = 1; w < kW; ++w) {
-      lse_merge(st.M, st.S, sm[w][n], ss[w][n]);
-      CandState o;
-      o.lo = slo[w][n];
-      o.hi1 = shi1[w][n];
-      o.hi2 = shi2[w][n];
-      o.b1 = sb1[w][n];
-      st.cand.merge(o);
+  if constexpr (MODE == kModeDraft) {
+    __shared__ float sm[kW][32], slo[kW][32], shi1[kW][32], shi2[kW][32];
+    __shared__ double ss[kW][32];
+    __shared__ int sb1[kW][32];
+    if (h == 0) {
+      sm[wave][n] = st.M;
+      ss[wave][n] = st.S;
+      slo[wave][n] = st.cand.lo;
+      shi1[wave][n] = st.cand.hi1;
+      shi2[wave][n] = st.cand.hi2;
+      sb1[wave][n] = st.cand.b1;
     }
-    finish<kModeDraft>(st, rc, n, split, a, h == 0);
+    __syncthreads();
+    if (wave == 0) {
+      for (int w = 1; w < kW; ++w) {
+        lse_merge(st.M, st.S, sm[w][n], ss[w][n]);
+        CandState o;
+        o.lo = slo[w][n];
+        o.hi1 = shi1[w][n];
+        o.hi2 = shi2[w][n];
+        o.b1 = sb1[w][n];
+        st.cand.merge(o);
+      }
+      finish<MODE>(st, rc, n, split, a, h == 0);
+    }
+  } else {
+    __shared__ CandState sc[kW][32], sf[kW][32];
+    __shared__ float sw[kW][32];
+    if (h == 0) {
+      sc[wave][n] = st.cand;
+      sf[wave][n] = st.candf;
+      sw[wave][n] = st.wpos;
+    }
+    __syncthreads();
+    if (wave == 0) {
+      for (int w = 1; w < kW; ++w) {
+        st.cand.merge(sc[w][n]);
+        st.candf.merge(sf[w][n]);
+        st.wpos += sw[w][n];
+      }
+      finish<MODE>(st, rc, n, split, a, h == 0);
+    }
   }
 }
 
@@ -799,7 +838,7 @@ BiasGeometry bias_geometry(int mode, bool bf16, int nrows, int V) {
   return g;
 }
 
-int small_draft_splits(int nrows, int V) {
+int small_pass_splits(int nrows, int V) {
   const int ntiles = (V + kTile - 1) / kTile;
   return nrows <= 32 ? min(ntiles, 256) : 0;
 }
@@ -808,13 +847,21 @@ hipError_t launch_bias_pass(int mode, bool bf16, const BiasPassArgs& a, hipStrea
   TimingScope timing(mode == kModeDraft ? "draft_bias" : (mode == kModeCstar ? "cstar_bias" : "residual_bias"), stream);
   const dim3 grid(a.nsplit, (a.nrows + kRowsPerBlock - 1) / kRowsPerBlock);
   const dim3 block(kThreads);
-  if (bf16 && mode == kModeDraft && a.tiles_per_stage == 1) {  // at most 32 rows
+  if (bf16 && mode != kModeCstar && a.tiles_per_stage == 1) {  // at most 32 rows
     if (a.nrows > 32) return hipErrorInvalidValue;
     const dim3 g(a.nsplit), b(256);
-    if (a.vec_ok && a.zout) hipLaunchKernelGGL((k_bias_small<true, true>), g, b, 0, stream, a);
-    else if (a.vec_ok) hipLaunchKernelGGL((k_bias_small<true, false>), g, b, 0, stream, a);
-    else if (a.zout) hipLaunchKernelGGL((k_bias_small<false, true>), g, b, 0, stream, a);
-    else hipLaunchKernelGGL((k_bias_small<false, false>), g, b, 0, stream, a);
+    if (mode == kModeResidual) {
+      if (a.vec_ok) hipLaunchKernelGGL((k_bias_small<kModeResidual, true, false>), g, b, 0, stream, a);
+      else hipLaunchKernelGGL((k_bias_small<kModeResidual, false, false>), g, b, 0, stream, a);
+    } else if (a.vec_ok && a.zout) {
+      hipLaunchKernelGGL((k_bias_small<kModeDraft, true, true>), g, b, 0, stream, a);
+    } else if (a.vec_ok) {
+      hipLaunchKernelGGL((k_bias_small<kModeDraft, true, false>), g, b, 0, stream, a);
+    } else if (a.zout) {
+      hipLaunchKernelGGL((k_bias_small<kModeDraft, false, true>), g, b, 0, stream, a);
+    } else {
+      hipLaunchKernelGGL((k_bias_small<kModeDraft, false, false>), g, b, 0, stream, a);
+    }
   } else if (bf16 && mode == kModeDraft && a.zout) {
     if (a.vec_ok) hipLaunchKernelGGL((k_bias_bf16<kModeDraft, 2, true, true>), grid, block, 0, stream, a);
     else hipLaunchKernelGGL((k_bias_bf16<kModeDraft, 2, false, true>), grid, block, 0, stream, a);

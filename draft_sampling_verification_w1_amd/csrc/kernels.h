@@ -107,9 +107,9 @@ struct BiasGeometry {
   int nsplit;
 };
 BiasGeometry bias_geometry(int mode, bool bf16, int nrows, int V);
-// Draft splits of the small-batch pass (at most 32 rows, bf16; tile-granular
+// Splits of the small-batch draft and residual passes (at most 32 rows, bf16; tile-granular
 // splits, one per workgroup), or 0 when the batch is larger.
-int small_draft_splits(int nrows, int V);
+int small_pass_splits(int nrows, int V);
 
 // First tile of split `s` of a pass with `nsplit` splits over ntiles tiles
 // grouped in stages of `tps` tiles (split s covers [split_tile(s), split_tile(s+1))).
