@@ -127,39 +127,46 @@ __device__ __forceinline__ float bf16_at(const uint16_t* p, int64_t i) {
   return __uint_as_float((uint32_t)p[i] << 16);
 }
 
-// Load 16 consecutive elements [v, v+16) of a row into floats; entries at or
-// beyond V read as -inf.  `vec_ok` (row base 16-byte aligned) enables vector loads.
-__device__ __forceinline__ void load16(const uint16_t* row, int v, int V, bool vec_ok, float* out) {
-  if (vec_ok && v + 16 <= V) {
-    const u32x4* p = reinterpret_cast<const u32x4*>(row + v);
-    const u32x4 a = __builtin_nontemporal_load(p);
-    const u32x4 b = __builtin_nontemporal_load(p + 1);
-    const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+// A thread's 16 elements of a 4,096-element slice [base, base + 4096) of a
+// row read by a 256-thread workgroup: 16-byte groups at base + E tid + 256 E g
+// (E = elements per 16 bytes, g < 16 / E), so that each load instruction of a
+// wave covers one contiguous kilobyte.  Entries at or beyond `end` read as
+// -inf.  `vec_ok` (row base 16-byte aligned) enables vector loads.
+__device__ __forceinline__ void load_slice16(const uint16_t* row, int base, int tid, int end,
+                                             bool vec_ok, float* out) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      out[2 * i] = bf16_lo(w[i]);
-      out[2 * i + 1] = bf16_hi(w[i]);
+  for (int g = 0; g < 2; ++g) {
+    const int v = base + 8 * tid + 2048 * g;
+    if (vec_ok && v + 8 <= end) {
+      const u32x4 a = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(row + v));
+      const uint32_t w[4] = {a.x, a.y, a.z, a.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        out[8 * g + 2 * i] = bf16_lo(w[i]);
+        out[8 * g + 2 * i + 1] = bf16_hi(w[i]);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) out[8 * g + i] = (v + i < end) ? bf16_at(row, v + i) : -INFINITY;
     }
-  } else {
-#pragma unroll
-    for (int i = 0; i < 16; ++i) out[i] = (v + i < V) ? bf16_at(row, v + i) : -INFINITY;
   }
 }
 
-__device__ __forceinline__ void load16(const float* row, int v, int V, bool vec_ok, float* out) {
-  if (vec_ok && v + 16 <= V) {
-    const f32x4* p = reinterpret_cast<const f32x4*>(row + v);
+__device__ __forceinline__ void load_slice16(const float* row, int base, int tid, int end,
+                                             bool vec_ok, float* out) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const f32x4 q = __builtin_nontemporal_load(p + i);
-      out[4 * i] = q.x;
-      out[4 * i + 1] = q.y;
-      out[4 * i + 2] = q.z;
-      out[4 * i + 3] = q.w;
+  for (int g = 0; g < 4; ++g) {
+    const int v = base + 4 * tid + 1024 * g;
+    if (vec_ok && v + 4 <= end) {
+      const f32x4 q = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(row + v));
+      out[4 * g] = q.x;
+      out[4 * g + 1] = q.y;
+      out[4 * g + 2] = q.z;
+      out[4 * g + 3] = q.w;
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) out[4 * g + i] = (v + i < end) ? row[v + i] : -INFINITY;
     }
-  } else {
-#pragma unroll
-    for (int i = 0; i < 16; ++i) out[i] = (v + i < V) ? row[v + i] : -INFINITY;
   }
 }
 

@@ -129,9 +129,9 @@ __global__ __launch_bounds__(256) void k_target_lse(int gamma, int V, const E* T
   // error of L only.
   float m = -INFINITY, kf = 0.f;
   double s = 0.0;
-  for (int v = v0 + 16 * threadIdx.x; v < v1; v += 16 * 256) {
+  for (int v = v0; v < v1; v += 16 * 256) {
     float x[16];
-    load16(row, v, v1, vec_ok, x);
+    load_slice16(row, v, (int)threadIdx.x, v1, vec_ok, x);
     float mt = x[0];
 #pragma unroll
     for (int j = 1; j < 16; ++j) mt = fmaxf(mt, x[j]);
