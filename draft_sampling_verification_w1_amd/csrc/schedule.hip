@@ -65,88 +65,27 @@ __device__ int64_t block_exclusive_scan(int64_t v, int64_t* wsum, int64_t& total
   return before + x - v;
 }
 
-// E candidates per thread (E * 1024 >= R * gamma).  MODE: kAlg1 (causal
-// stop), kCapacity (argmax of Theta over the whole path; K written to
-// k_io[0]), kTopK (the first min(k_io[0], R*gamma) candidates).
-template <int E, int MODE>
-__global__ __launch_bounds__(kThreads) void k_schedule(int R, int gamma, const float* c,
-                                                       const float* sps, float* a_out,
-                                                       int32_t* lengths, double* stats,
-                                                       double* theta_path, int32_t* k_io) {
-  __shared__ uint64_t keys[kMaxCand];
-  __shared__ int cnt[64 * kWaves];
-  __shared__ int64_t wsum[kWaves];
-  __shared__ int first_stop;
-  __shared__ unsigned long long best_bits;
+// Stable LSD radix sort of ks[0 .. EE * 1024) on the 30 bits of
+// survival_key_hi (bits 32..61 of the key), 6 bits (64 digits) per pass.
+// Wave w holds positions w*64EE + q*64 + lane (q < EE), so the order
+// (wave, q, lane) is the position order.  A key's new place = the offset of
+// (its digit, its wave) + the keys of that digit before it in the wave.
+// Ballots of the digit bits give each lane the lanes of its q with the same
+// digit; the lowest of them adds the group to the wave's counter of that
+// digit (cnt[digit][wave], touched by this wave alone, in program order) and
+// hands the previous count to the group.
+template <int EE>
+__device__ __forceinline__ void radix_sort(uint64_t* ks, int* cnt, int64_t* wsum) {
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
-  const int n = R * gamma;
-  constexpr int npad = E * kThreads;
-  const int base = E * tid;  // the thread's sorted positions base .. base + E - 1
-
-  // the stop test's table entries SPS(R + i) for i = base - 1 .. base + E - 1:
-  // their positions are known now, so the loads overlap the sort (at E = 16
-  // the registers are short, and they are loaded where they are used)
-  constexpr bool kEarly = E <= 8;
-  float sp[kEarly ? E + 1 : 1];
-  if constexpr (kEarly) {
-#pragma unroll
-    for (int q = 0; q <= E; ++q) sp[q] = (base + q <= n) ? sps[R + base + q - 1] : 0.0f;
-  }
-  auto sps_at = [&](int q) -> float {
-    if constexpr (kEarly) return sp[q];
-    else return sps[R + base + q - 1];
-  };
-  const float sps_r = sps[R - 1];
-
-  // prefix products, one request per thread (sequential binary32 multiplies;
-  // a request's factors are fetched together, 16 at a time); the key of
-  // candidate o = r * gamma + j sits at position o
-  for (int r = tid; r < R; r += kThreads) {
-    const int o0 = r * gamma;
-    float acc = 1.0f;
-    for (int j0 = 0; j0 < gamma; j0 += 16) {
-      float cc[16];
-#pragma unroll
-      for (int u = 0; u < 16; ++u) cc[u] = (j0 + u < gamma) ? c[o0 + j0 + u] : 1.0f;
-#pragma unroll
-      for (int u = 0; u < 16; ++u) {
-        if (j0 + u < gamma) {
-          const int o = o0 + j0 + u;
-          acc = __fmul_rn(acc, cc[u]);
-          a_out[o] = acc;
-          keys[o] = ((uint64_t)survival_key_hi(acc) << 32) | (uint32_t)o;
-        }
-      }
-    }
-  }
-  for (int p = n + tid; p < npad; p += kThreads) keys[p] = ~(uint64_t)0;  // after every real key
-  if (tid == 0) {
-    // kTopK: the count handed over (clamped to [0, n]); otherwise n = "no stop yet"
-    int k0 = n;
-    if constexpr (MODE == kTopK) k0 = min(max(k_io[0], 0), n);
-    first_stop = k0;
-    // Theta >= 0 (a, SPS >= 0), so the bit patterns of the doubles order as the values
-    best_bits = (unsigned long long)__double_as_longlong((double)R * (double)sps_r);
-  }
-  __syncthreads();
-
-  // stable LSD radix sort on the 30 bits of survival_key_hi, 6 bits (64 digits)
-  // per pass.  Wave w holds positions w*64E + q*64 + lane (q < E), so the
-  // order (wave, q, lane) is the position order.  A key's new place = the
-  // offset of (its digit, its wave) + the keys of that digit before it in the
-  // wave.  Ballots of the digit bits give each lane the lanes of its q with
-  // the same digit; the lowest of them adds the group to the wave's counter of
-  // that digit (cnt[digit][wave], touched by this wave alone, in program
-  // order) and hands the previous count to the group.
   const uint64_t below = (1ull << lane) - 1ull;
   for (int shift = 32; shift < 62; shift += 6) {
-    uint64_t e[E];
-    int dig[E], rank[E];
+    uint64_t e[EE];
+    int dig[EE], rank[EE];
     cnt[lane * kWaves + wave] = 0;  // digit = lane
 #pragma unroll
-    for (int q = 0; q < E; ++q) {
-      e[q] = keys[wave * 64 * E + q * 64 + lane];
+    for (int q = 0; q < EE; ++q) {
+      e[q] = ks[wave * 64 * EE + q * 64 + lane];
       const int d = (int)(e[q] >> shift) & 63;
       dig[q] = d;
       uint64_t same = ~0ull;
@@ -168,80 +107,119 @@ __global__ __launch_bounds__(kThreads) void k_schedule(int R, int gamma, const f
     cnt[tid] = (int)off;
     __syncthreads();
 #pragma unroll
-    for (int q = 0; q < E; ++q) keys[cnt[dig[q] * kWaves + wave] + rank[q]] = e[q];
+    for (int q = 0; q < EE; ++q) ks[cnt[dig[q] * kWaves + wave] + rank[q]] = e[q];
     __syncthreads();
   }
-  uint64_t e[E];
+}
+
+struct SchedShared {
+  int64_t wsum[kWaves];
+  int first_stop;
+  int head_n;
+  unsigned long long best_bits;
+};
+
+// The rest of a schedule once ks[0 .. m) holds the first m candidates of the
+// survival order (thread t owns places EE t .. EE t + EE - 1; sp[q] is
+// SPS(R + EE t + q), B = R + i candidates before place i): the exact tau scan,
+// the stop (MODE), lengths, statistics and the Theta path.  With `head` set,
+// ks holds only the first m of n candidates; if the stop is not decided
+// within them the call writes nothing and returns false.  The per-request
+// lengths are gathered in `len_area` (free once the keys are in registers).
+template <int EE, int MODE>
+__device__ __forceinline__ bool finish_schedule(const uint64_t* ks, int m, bool head, int R,
+                                                int gamma, int n, const float* sps,
+                                                const float (&sp)[EE + 1], float sps_r,
+                                                void* len_area, SchedShared& sh, int32_t* lengths,
+                                                double* stats, double* theta_path, int32_t* k_io) {
+  constexpr bool kEarly = EE <= 8;
+  const int tid = threadIdx.x;
+  const int base = EE * tid;
+#define SPS_AT(q) (kEarly ? sp[(q)] : sps[R + base + (q) - 1])
+  if (tid == 0) {
+    // kTopK: the count handed over (clamped to [0, n]); otherwise "no stop yet"
+    int k0 = m;
+    if constexpr (MODE == kTopK) k0 = min(max(k_io[0], 0), n);
+    sh.first_stop = k0;
+    // Theta >= 0 (a, SPS >= 0), so the bit patterns of the doubles order as the values
+    sh.best_bits = (unsigned long long)__double_as_longlong((double)R * (double)sps_r);
+  }
+  uint64_t e[EE];
 #pragma unroll
-  for (int q = 0; q < E; ++q) e[q] = base + q < n ? keys[base + q] : ~(uint64_t)0;
+  for (int q = 0; q < EE; ++q) e[q] = base + q < m ? ks[base + q] : ~(uint64_t)0;
 
   // exact tau increments and their workgroup scan
   int64_t local = 0;
 #pragma unroll
-  for (int q = 0; q < E; ++q) local += base + q < n ? tau_unit(e[q]) : 0;
+  for (int q = 0; q < EE; ++q) local += base + q < m ? tau_unit(e[q]) : 0;
   int64_t total;
-  const int64_t offset = block_exclusive_scan(local, wsum, total);
-  // every thread has its keys in registers now (the scan's barrier): the key
-  // array holds the per-request lengths from here on
-  int* len = reinterpret_cast<int*>(keys);
-  for (int r = tid; r < R; r += kThreads) len[r] = 0;
+  const int64_t offset = block_exclusive_scan(local, sh.wsum, total);
   const int64_t tau0 = (int64_t)R << 38;
   const double theta0 = (double)R * (double)sps_r;
-  int64_t tau = tau0 + offset;  // before element base
+  int64_t tau = tau0 + offset;  // before place base
   if constexpr (MODE == kAlg1) {
-    int my_stop = n;
+    int my_stop = m;
 #pragma unroll
-    for (int q = 0; q < E; ++q) {
+    for (int q = 0; q < EE; ++q) {
       const int i = base + q;
-      if (i < n) {
-        const double before = ldexp((double)tau, -38) * (double)sps_at(q);
+      if (i < m) {
+        const double before = ldexp((double)tau, -38) * (double)SPS_AT(q);
         tau += tau_unit(e[q]);
-        const double after = ldexp((double)tau, -38) * (double)sps_at(q + 1);
-        if (!(after > before) && my_stop == n) my_stop = i;
+        const double after = ldexp((double)tau, -38) * (double)SPS_AT(q + 1);
+        if (!(after > before) && my_stop == m) my_stop = i;
       }
     }
-    if (my_stop < n) atomicMin(&first_stop, my_stop);
+    if (my_stop < m) atomicMin(&sh.first_stop, my_stop);
   } else if constexpr (MODE == kCapacity) {
     // the largest Theta after any count i + 1 = 1..n (count 0 seeded above),
     // then the smallest count that reaches it
-    double th[E];
+    double th[EE];
     double mx = 0.0;
 #pragma unroll
-    for (int q = 0; q < E; ++q) {
+    for (int q = 0; q < EE; ++q) {
       const int i = base + q;
       th[q] = -1.0;
-      if (i < n) {
+      if (i < m) {
         tau += tau_unit(e[q]);
-        th[q] = ldexp((double)tau, -38) * (double)sps_at(q + 1);
+        th[q] = ldexp((double)tau, -38) * (double)SPS_AT(q + 1);
         mx = fmax(mx, th[q]);
       }
     }
-    atomicMax(&best_bits, (unsigned long long)__double_as_longlong(mx));
+    atomicMax(&sh.best_bits, (unsigned long long)__double_as_longlong(mx));
     __syncthreads();
-    const double best = __longlong_as_double((long long)best_bits);
-    if (tid == 0 && (double)R * (double)sps_r == best) atomicMin(&first_stop, 0);
+    const double best = __longlong_as_double((long long)sh.best_bits);
+    if (tid == 0 && (double)R * (double)sps_r == best) atomicMin(&sh.first_stop, 0);
 #pragma unroll
-    for (int q = 0; q < E; ++q)
+    for (int q = 0; q < EE; ++q)
       if (th[q] == best) {
-        atomicMin(&first_stop, base + q + 1);
+        atomicMin(&sh.first_stop, base + q + 1);
         break;
       }
   }
   __syncthreads();
-  const int sel = first_stop;
+  const int sel = sh.first_stop;
+  // Algorithm 1 decides its stop at place sel from places 0..sel, so the head
+  // must hold place sel; a top-K count needs places 0..K-1 only
+  if (head && (MODE == kAlg1 ? sel >= m : sel > m)) {
+    __syncthreads();  // every thread has read first_stop
+    return false;
+  }
   if constexpr (MODE == kCapacity) {
     if (tid == 0) k_io[0] = sel;
   }
+  int* len = reinterpret_cast<int*>(len_area);
+  for (int r = tid; r < R; r += kThreads) len[r] = 0;
+  __syncthreads();
 
   // lengths: every selected candidate raises its request's length
   tau = tau0 + offset;
 #pragma unroll
-  for (int q = 0; q < E; ++q) {
+  for (int q = 0; q < EE; ++q) {
     const int i = base + q;
-    if (i < n) {
+    if (i < m) {
       const uint32_t o = (uint32_t)e[q];
       tau += tau_unit(e[q]);
-      const double th = ldexp((double)tau, -38) * (double)sps_at(q + 1);
+      const double th = ldexp((double)tau, -38) * (double)SPS_AT(q + 1);
       if (i < sel) atomicMax(&len[o / gamma], (int)(o % gamma) + 1);
       // Algorithm 1 records the path up to and including the stopping step;
       // the capacity search records all of it
@@ -254,6 +232,8 @@ __global__ __launch_bounds__(kThreads) void k_schedule(int R, int gamma, const f
       }
     }
   }
+  if (theta_path)
+    for (int i = m + tid; i < n; i += kThreads) theta_path[i + 1] = NAN;  // past the head
   __syncthreads();
   for (int r = tid; r < R; r += kThreads) lengths[r] = len[r];
   if (tid == 0) {
@@ -265,6 +245,123 @@ __global__ __launch_bounds__(kThreads) void k_schedule(int R, int gamma, const f
       stats[3] = 0.0;
     }
   }
+  return true;
+}
+#undef SPS_AT
+
+// E candidates per thread (E * 1024 >= R * gamma).  MODE: kAlg1 (causal
+// stop), kCapacity (argmax of Theta over the whole path; K written to
+// k_io[0]), kTopK (the first min(k_io[0], R*gamma) candidates).
+//
+// Head of the order (kAlg1 and kTopK, more than 1024 candidates): Algorithm 1
+// usually stops after a small part of the candidates (about one position per
+// request where SPS bends at twice the batch), and a top-K count is usually
+// small too.  A histogram of the top 10 key bits finds the longest run of
+// leading buckets holding at most 1024 candidates; every other candidate has
+// a larger key, so those candidates sorted are exactly the first places of
+// the full order.  They are sorted alone (one per thread), and the full sort
+// runs only when the stop or the count lies beyond them.
+template <int E, int MODE>
+__global__ __launch_bounds__(kThreads) void k_schedule(int R, int gamma, const float* c,
+                                                       const float* sps, float* a_out,
+                                                       int32_t* lengths, double* stats,
+                                                       double* theta_path, int32_t* k_io) {
+  constexpr bool kHead = MODE != kCapacity && E >= 2;
+  __shared__ uint64_t keys[kMaxCand];
+  __shared__ int cnt[64 * kWaves];
+  __shared__ uint64_t head_keys[kHead ? kThreads : 1];
+  __shared__ int hist[kHead ? kThreads : 1];
+  __shared__ SchedShared sh;
+  const int tid = threadIdx.x;
+  const int n = R * gamma;
+  constexpr int npad = E * kThreads;
+  const int base = E * tid;  // the thread's sorted places base .. base + E - 1
+
+  // the stop test's table entries SPS(R + i) for i = base - 1 .. base + E - 1:
+  // their places are known now, so the loads overlap the sort (at E = 16
+  // the registers are short, and they are loaded where they are used)
+  constexpr bool kEarly = E <= 8;
+  float sp[E + 1];
+  if constexpr (kEarly) {
+#pragma unroll
+    for (int q = 0; q <= E; ++q) sp[q] = (base + q <= n) ? sps[R + base + q - 1] : 0.0f;
+  }
+  // the head's places are tid (n > 1024 here, so both entries exist)
+  float sp1[2] = {0.0f, 0.0f};
+  if constexpr (kHead && kEarly) {
+    sp1[0] = sps[R + tid - 1];
+    sp1[1] = sps[R + tid];
+  }
+  const float sps_r = sps[R - 1];
+
+  // prefix products, one request per thread (sequential binary32 multiplies;
+  // a request's factors are fetched together, 16 at a time); the key of
+  // candidate o = r * gamma + j sits at place o
+  for (int r = tid; r < R; r += kThreads) {
+    const int o0 = r * gamma;
+    float acc = 1.0f;
+    for (int j0 = 0; j0 < gamma; j0 += 16) {
+      float cc[16];
+#pragma unroll
+      for (int u = 0; u < 16; ++u) cc[u] = (j0 + u < gamma) ? c[o0 + j0 + u] : 1.0f;
+#pragma unroll
+      for (int u = 0; u < 16; ++u) {
+        if (j0 + u < gamma) {
+          const int o = o0 + j0 + u;
+          acc = __fmul_rn(acc, cc[u]);
+          a_out[o] = acc;
+          keys[o] = ((uint64_t)survival_key_hi(acc) << 32) | (uint32_t)o;
+        }
+      }
+    }
+  }
+  for (int p = n + tid; p < npad; p += kThreads) keys[p] = ~(uint64_t)0;  // after every real key
+  if constexpr (kHead) hist[tid] = 0;
+  __syncthreads();
+
+  if constexpr (kHead) {
+    // bucket = key >> 52: the top 10 of the 30 survival-key bits
+#pragma unroll
+    for (int q = 0; q < E; ++q)
+      if (base + q < n) atomicAdd(&hist[(int)(keys[base + q] >> 52)], 1);
+    __syncthreads();
+    int64_t tot;
+    const int h = hist[tid];
+    const int64_t incl = block_exclusive_scan(h, sh.wsum, tot) + h;  // candidates in buckets <= tid
+    hist[tid] = incl <= kThreads ? 1 : 0;  // bucket in the head
+    if (tid == 0) sh.head_n = 0;
+    __syncthreads();
+    if (incl <= kThreads) atomicMax(&sh.head_n, (int)incl);
+    __syncthreads();
+    const int m = sh.head_n;
+    if (m > 0) {
+      // the head's keys in place order (equal keys keep their (r, j) order)
+      bool in[E];
+      int mine = 0;
+#pragma unroll
+      for (int q = 0; q < E; ++q) {
+        in[q] = base + q < n && hist[(int)(keys[base + q] >> 52)] != 0;
+        mine += in[q] ? 1 : 0;
+      }
+      int w = (int)block_exclusive_scan(mine, sh.wsum, tot);
+#pragma unroll
+      for (int q = 0; q < E; ++q)
+        if (in[q]) head_keys[w++] = keys[base + q];
+      if (tid >= m) head_keys[tid] = ~(uint64_t)0;
+      __syncthreads();
+      radix_sort<1>(head_keys, cnt, sh.wsum);
+      if constexpr (!kEarly) {
+        sp1[0] = sps[R + tid - 1];
+        sp1[1] = sps[R + tid];
+      }
+      if (finish_schedule<1, MODE>(head_keys, m, true, R, gamma, n, sps, sp1, sps_r, keys, sh,
+                                   lengths, stats, theta_path, k_io))
+        return;
+    }
+  }
+  radix_sort<E>(keys, cnt, sh.wsum);
+  finish_schedule<E, MODE>(keys, n, false, R, gamma, n, sps, sp, sps_r, keys, sh, lengths, stats,
+                           theta_path, k_io);
 }
 
 }  // namespace
