@@ -328,6 +328,54 @@ def test_schedule_ties(dev, R, gamma):
         assert 0 < n_sel < R * gamma, f"stop at {n_sel}: the cut is not exercised"
 
 
+def _head_size(a):
+    """Candidates in the longest run of leading buckets (top 10 bits of the
+    30-bit survival key 0x3F800000 - bits(a)) holding at most 1024 of them:
+    the part of the survival order the scheduler sorts first when there are
+    more than 1024 candidates.  Used only to pick cases on either side of
+    that boundary; the results are compared with the oracle's whatever it is."""
+    b = a.ravel().astype(np.float32).view(np.uint32).astype(np.int64)
+    key = np.where(b & 0x80000000, 0x3F800000, np.where(b > 0x3F800000, 0, 0x3F800000 - b))
+    incl = np.cumsum(np.bincount(key >> 20, minlength=1024))
+    return int(incl[incl <= 1024].max()) if (incl <= 1024).any() else 0
+
+
+@pytest.mark.parametrize("R,gamma", [(100, 13), (256, 16), (600, 16), (1024, 16)])
+def test_schedule_head_of_order(dev, R, gamma):
+    """Algorithm 1 stopping at chosen places around the end of the head of the
+    survival order (an SPS table flat up to B = R + p and tiny after it stops
+    at place p), and top-K counts around it: lengths, statistics and the Theta
+    path equal the oracle's whether or not the stop lies inside the head.
+    R*gamma > 8192 runs 16 keys per thread."""
+    import torch
+    from oracle import oracle as O
+    rng = np.random.default_rng(R + gamma)
+    n = R * gamma
+    c = rng.uniform(0.3, 1.0, (R, gamma)).astype(np.float32)
+    c[3] = c[5]  # equal keys across requests
+    a = O.prefix_products(c)
+    h = _head_size(a)
+    assert 0 < h < n
+    for p in sorted({0, 1, h // 2, h - 1, h, h + 1, min(2 * h, n - 1)}):
+        sps = np.full(R + n, 1000.0, np.float32)
+        sps[R + p:] = 1.0  # SPS(B) = sps[B - 1]: the step to B = R + p + 1 loses
+        os_ = O.schedule(a, sps)
+        assert int(os_["stats"][3]) == p
+        gs = dev.schedule(to_dev(c), to_dev(sps))
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(gs["a"].cpu().numpy(), a)
+        np.testing.assert_array_equal(gs["lengths"].cpu().numpy(), os_["lengths"])
+        np.testing.assert_array_equal(gs["stats"].cpu().numpy(), os_["stats"])
+        np.testing.assert_array_equal(gs["theta_path"].cpu().numpy(), os_["theta_path"])
+    sps = np.full(R + n, 100.0, np.float32)
+    for K in sorted({0, 1, h - 1, h, h + 1, n - 1, n}):
+        ot = O.schedule_topk(a, sps, K)
+        gt = dev.schedule_topk(to_dev(c), to_dev(np.array([K], np.int32)), to_dev(sps))
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(gt["lengths"].cpu().numpy(), ot["lengths"])
+        np.testing.assert_array_equal(gt["stats"].cpu().numpy(), ot["stats"])
+
+
 def test_schedule_factor_above_one(dev):
     """A factor just above 1 (a c* rounded up past 1, say) makes a request's
     products rise by an ulp, so its positions are no longer in key order.  The
