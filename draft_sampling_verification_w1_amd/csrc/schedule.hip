@@ -8,7 +8,8 @@
 // One workgroup of 1024 threads: binary32 products per request, a stable
 // radix sort of the candidates by survival (ties keep the (r, j) order), an
 // exact integer scan of tau (units of 2^-38) and a parallel search for the
-// first non-improving step.
+// first non-improving step.  Above 1024 candidates the stop is first sought
+// in the head of the survival order alone (k_schedule).
 //
 // The same kernel serves the production variant (summary page §5.2): the
 // capacity K of a later round is the candidate count with the largest Theta
