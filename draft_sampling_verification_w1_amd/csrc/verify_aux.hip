@@ -259,27 +259,48 @@ __global__ __launch_bounds__(256) void k_bonus(int gamma, int V, uint64_t seed, 
   const bool vec_ok = w.vec_ok != 0;
   CandState cs;
   cs.init();
-  for (int v = t0 * kTile + 8 * (int)threadIdx.x; v < t1 * kTile; v += 8 * 256) {
-    float x[8];
-    load8(row, v, V, vec_ok, x);
-    float m = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])), fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
-    m = fmaxf(m, __shfl_xor(m, 1, 64));
-    m = fmaxf(m, __shfl_xor(m, 2, 64));
-    float s = 0.f;
-    if (m > -INFINITY) {
-      float e[8];
+  // Four 2048-token steps per iteration.  In every step the quad of a block
+  // reduces its maximum and sum; thread q of the quad keeps step q's block, so
+  // the per-block work (Philox block, Gumbel variate, logarithm, record) runs
+  // on every lane once per four steps rather than on one lane in four per step.
+  // The record keeps the largest bounds whatever the order the blocks come in
+  // (an exact tie of upper bounds leaves hi2 = hi1, and every block of the
+  // split is then rescored).
+  const int vend = t1 * kTile;  // a multiple of 32: a quad is in or out as a whole
+  const int q4 = (int)threadIdx.x & 3;
+  for (int v0 = t0 * kTile + 8 * (int)threadIdx.x; v0 < vend; v0 += 4 * 8 * 256) {
+    float km = -INFINITY, ks = 0.f;
+    int kblk = -1;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) e[j] = __builtin_amdgcn_exp2f((x[j] - m) * kLog2e);
-      s = ((e[0] + e[1]) + (e[2] + e[3])) + ((e[4] + e[5]) + (e[6] + e[7]));
+    for (int u = 0; u < 4; ++u) {
+      const int v = v0 + u * 8 * 256;
+      if (v < vend) {
+        float x[8];
+        load8(row, v, V, vec_ok, x);
+        float m = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])), fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
+        m = fmaxf(m, __shfl_xor(m, 1, 64));
+        m = fmaxf(m, __shfl_xor(m, 2, 64));
+        float s = 0.f;
+        if (m > -INFINITY) {
+          float e[8];
+#pragma unroll
+          for (int j = 0; j < 8; ++j) e[j] = __builtin_amdgcn_exp2f((x[j] - m) * kLog2e);
+          s = ((e[0] + e[1]) + (e[2] + e[3])) + ((e[4] + e[5]) + (e[6] + e[7]));
+        }
+        s += __shfl_xor(s, 1, 64);
+        s += __shfl_xor(s, 2, 64);
+        if (q4 == u) {
+          km = m;
+          ks = s;
+          kblk = v / kTile;
+        }
+      }
     }
-    s += __shfl_xor(s, 1, 64);
-    s += __shfl_xor(s, 2, 64);
-    if ((threadIdx.x & 3) == 0 && m > -INFINITY) {
-      const int blk = v / kTile;
-      const u32x4 words = noise_block(seed, kStreamBonus, r, kb, (uint32_t)blk >> 2);
-      const float sc = fmaf(__builtin_amdgcn_logf(s), kLn2, m) + gumbel_f32(word_of(words, blk & 3));
-      const float d = fmaf(kScoreRel, fabsf(m), kScoreAbs);
-      cs.add(sc - d, sc + d, blk);
+    if (kblk >= 0 && km > -INFINITY) {
+      const u32x4 words = noise_block(seed, kStreamBonus, r, kb, (uint32_t)kblk >> 2);
+      const float sc = fmaf(__builtin_amdgcn_logf(ks), kLn2, km) + gumbel_f32(word_of(words, kblk & 3));
+      const float d = fmaf(kScoreRel, fabsf(km), kScoreAbs);
+      cs.add(sc - d, sc + d, kblk);
     }
   }
 #pragma unroll
