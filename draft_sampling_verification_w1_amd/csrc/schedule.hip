@@ -66,6 +66,18 @@ __device__ int64_t block_exclusive_scan(int64_t v, int64_t* wsum, int64_t& total
   return before + x - v;
 }
 
+// Largest value over the wave (every lane gets it), so that a workgroup
+// maximum takes one LDS atomic per wave instead of one per thread on a single
+// address.
+__device__ __forceinline__ unsigned long long wave_max_u64(unsigned long long x) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    const unsigned long long y = __shfl_xor(x, off, 64);
+    x = y > x ? y : x;
+  }
+  return x;
+}
+
 // Stable LSD radix sort of ks[0 .. EE * 1024) on the 30 bits of
 // survival_key_hi (bits 32..61 of the key), 6 bits (64 digits) per pass.
 // Wave w holds positions w*64EE + q*64 + lane (q < EE), so the order
@@ -118,6 +130,7 @@ struct SchedShared {
   int first_stop;
   int head_n;
   unsigned long long best_bits;
+  unsigned long long umax, rest_bits;  // capacity head: largest tau unit outside, Theta bound
 };
 
 // The rest of a schedule once ks[0 .. m) holds the first m candidates of the
@@ -125,14 +138,16 @@ struct SchedShared {
 // SPS(R + EE t + q), B = R + i candidates before place i): the exact tau scan,
 // the stop (MODE), lengths, statistics and the Theta path.  With `head` set,
 // ks holds only the first m of n candidates; if the stop is not decided
-// within them the call writes nothing and returns false.  The per-request
+// within them the call writes nothing and returns false (for the capacity,
+// `rest_bound` bounds Theta at every count past the head).  The per-request
 // lengths are gathered in `len_area` (free once the keys are in registers).
 template <int EE, int MODE>
 __device__ __forceinline__ bool finish_schedule(const uint64_t* ks, int m, bool head, int R,
                                                 int gamma, int n, const float* sps,
                                                 const float (&sp)[EE + 1], float sps_r,
                                                 void* len_area, SchedShared& sh, int32_t* lengths,
-                                                double* stats, double* theta_path, int32_t* k_io) {
+                                                double* stats, double* theta_path, int32_t* k_io,
+                                                double rest_bound = 0.0) {
   constexpr bool kEarly = EE <= 8;
   const int tid = threadIdx.x;
   const int base = EE * tid;
@@ -158,6 +173,7 @@ __device__ __forceinline__ bool finish_schedule(const uint64_t* ks, int m, bool 
   const int64_t tau0 = (int64_t)R << 38;
   const double theta0 = (double)R * (double)sps_r;
   int64_t tau = tau0 + offset;  // before place base
+  double best = 0.0;
   if constexpr (MODE == kAlg1) {
     int my_stop = m;
 #pragma unroll
@@ -186,9 +202,10 @@ __device__ __forceinline__ bool finish_schedule(const uint64_t* ks, int m, bool 
         mx = fmax(mx, th[q]);
       }
     }
-    atomicMax(&sh.best_bits, (unsigned long long)__double_as_longlong(mx));
+    const unsigned long long mb = wave_max_u64((unsigned long long)__double_as_longlong(mx));
+    if ((tid & 63) == 0) atomicMax(&sh.best_bits, mb);
     __syncthreads();
-    const double best = __longlong_as_double((long long)sh.best_bits);
+    best = __longlong_as_double((long long)sh.best_bits);
     if (tid == 0 && (double)R * (double)sps_r == best) atomicMin(&sh.first_stop, 0);
 #pragma unroll
     for (int q = 0; q < EE; ++q)
@@ -200,9 +217,15 @@ __device__ __forceinline__ bool finish_schedule(const uint64_t* ks, int m, bool 
   __syncthreads();
   const int sel = sh.first_stop;
   // Algorithm 1 decides its stop at place sel from places 0..sel, so the head
-  // must hold place sel; a top-K count needs places 0..K-1 only
-  if (head && (MODE == kAlg1 ? sel >= m : sel > m)) {
-    __syncthreads();  // every thread has read first_stop
+  // must hold place sel; a top-K count needs places 0..K-1 only; the capacity
+  // holds when no count past the head can exceed the head's best Theta (one
+  // that only reaches it is not the smallest such count)
+  bool outside = false;
+  if constexpr (MODE == kAlg1) outside = sel >= m;
+  else if constexpr (MODE == kTopK) outside = sel > m;
+  else outside = rest_bound > best;
+  if (head && outside) {
+    __syncthreads();  // every thread has read first_stop and best_bits
     return false;
   }
   if constexpr (MODE == kCapacity) {
@@ -254,20 +277,25 @@ __device__ __forceinline__ bool finish_schedule(const uint64_t* ks, int m, bool 
 // stop), kCapacity (argmax of Theta over the whole path; K written to
 // k_io[0]), kTopK (the first min(k_io[0], R*gamma) candidates).
 //
-// Head of the order (kAlg1 and kTopK, more than 1024 candidates): Algorithm 1
-// usually stops after a small part of the candidates (about one position per
-// request where SPS bends at twice the batch), and a top-K count is usually
-// small too.  A histogram of the top 10 key bits finds the longest run of
-// leading buckets holding at most 1024 candidates; every other candidate has
-// a larger key, so those candidates sorted are exactly the first places of
-// the full order.  They are sorted alone (one per thread), and the full sort
-// runs only when the stop or the count lies beyond them.
+// Head of the order (more than 1024 candidates): Algorithm 1 usually stops
+// after a small part of the candidates (about one position per request where
+// SPS bends at twice the batch), and a top-K count is usually small too.  A
+// histogram of the top 10 key bits finds the longest run of leading buckets
+// holding at most 1024 candidates; every other candidate has a larger key, so
+// those candidates sorted are exactly the first places of the full order.
+// They are sorted alone (one per thread), and the full sort runs only when the
+// stop or the count lies beyond them.  The capacity (when no Theta path is
+// asked for) takes the head's best Theta when no later count can exceed it:
+// past the head, tau after c candidates is at most
+// min(tau(m) + (c - m) u_max, tau(n)) with u_max the largest tau unit outside
+// the head, and Theta(c) at most that bound times SPS(R + c), in the same
+// monotone binary64 arithmetic as Theta itself.
 template <int E, int MODE>
 __global__ __launch_bounds__(kThreads) void k_schedule(int R, int gamma, const float* c,
                                                        const float* sps, float* a_out,
                                                        int32_t* lengths, double* stats,
                                                        double* theta_path, int32_t* k_io) {
-  constexpr bool kHead = MODE != kCapacity && E >= 2;
+  constexpr bool kHead = E >= 2;
   __shared__ uint64_t keys[kMaxCand];
   __shared__ int cnt[64 * kWaves];
   __shared__ uint64_t head_keys[kHead ? kThreads : 1];
@@ -321,43 +349,81 @@ __global__ __launch_bounds__(kThreads) void k_schedule(int R, int gamma, const f
   __syncthreads();
 
   if constexpr (kHead) {
-    // bucket = key >> 52: the top 10 of the 30 survival-key bits
-#pragma unroll
-    for (int q = 0; q < E; ++q)
-      if (base + q < n) atomicAdd(&hist[(int)(keys[base + q] >> 52)], 1);
-    __syncthreads();
-    int64_t tot;
-    const int h = hist[tid];
-    const int64_t incl = block_exclusive_scan(h, sh.wsum, tot) + h;  // candidates in buckets <= tid
-    hist[tid] = incl <= kThreads ? 1 : 0;  // bucket in the head
-    if (tid == 0) sh.head_n = 0;
-    __syncthreads();
-    if (incl <= kThreads) atomicMax(&sh.head_n, (int)incl);
-    __syncthreads();
-    const int m = sh.head_n;
-    if (m > 0) {
-      // the head's keys in place order (equal keys keep their (r, j) order)
-      bool in[E];
-      int mine = 0;
-#pragma unroll
-      for (int q = 0; q < E; ++q) {
-        in[q] = base + q < n && hist[(int)(keys[base + q] >> 52)] != 0;
-        mine += in[q] ? 1 : 0;
-      }
-      int w = (int)block_exclusive_scan(mine, sh.wsum, tot);
+    if (MODE != kCapacity || theta_path == nullptr) {
+      // bucket = key >> 52: the top 10 of the 30 survival-key bits
 #pragma unroll
       for (int q = 0; q < E; ++q)
-        if (in[q]) head_keys[w++] = keys[base + q];
-      if (tid >= m) head_keys[tid] = ~(uint64_t)0;
+        if (base + q < n) atomicAdd(&hist[(int)(keys[base + q] >> 52)], 1);
       __syncthreads();
-      radix_sort<1>(head_keys, cnt, sh.wsum);
-      if constexpr (!kEarly) {
-        sp1[0] = sps[R + tid - 1];
-        sp1[1] = sps[R + tid];
+      int64_t tot;
+      const int h = hist[tid];
+      const int64_t incl = block_exclusive_scan(h, sh.wsum, tot) + h;  // candidates in buckets <= tid
+      hist[tid] = incl <= kThreads ? 1 : 0;  // bucket in the head
+      if (tid == 0) sh.head_n = 0;
+      __syncthreads();
+      const unsigned long long hn = wave_max_u64(incl <= kThreads ? (unsigned long long)incl : 0ull);
+      if ((tid & 63) == 0 && hn > 0) atomicMax(&sh.head_n, (int)hn);
+      __syncthreads();
+      const int m = sh.head_n;
+      if (m > 0) {
+        // the head's keys in place order (equal keys keep their (r, j) order)
+        bool in[E];
+        int mine = 0;
+        int64_t u_in = 0, u_all = 0;  // capacity: tau units of the head, of every candidate
+        unsigned long long u_out = 0;  // and the largest outside the head
+#pragma unroll
+        for (int q = 0; q < E; ++q) {
+          in[q] = base + q < n && hist[(int)(keys[base + q] >> 52)] != 0;
+          mine += in[q] ? 1 : 0;
+          if constexpr (MODE == kCapacity) {
+            if (base + q < n) {
+              const int64_t u = tau_unit(keys[base + q]);
+              u_all += u;
+              if (in[q]) u_in += u;
+              else u_out = max(u_out, (unsigned long long)u);
+            }
+          }
+        }
+        int w = (int)block_exclusive_scan(mine, sh.wsum, tot);
+#pragma unroll
+        for (int q = 0; q < E; ++q)
+          if (in[q]) head_keys[w++] = keys[base + q];
+        if (tid >= m) head_keys[tid] = ~(uint64_t)0;
+        __syncthreads();
+        radix_sort<1>(head_keys, cnt, sh.wsum);
+        if constexpr (!kEarly) {
+          sp1[0] = sps[R + tid - 1];
+          sp1[1] = sps[R + tid];
+        }
+        double rest_bound = 0.0;
+        if constexpr (MODE == kCapacity) {
+          if (tid == 0) {
+            sh.umax = 0ull;
+            sh.rest_bits = 0ull;
+          }
+          __syncthreads();
+          u_out = wave_max_u64(u_out);
+        if ((tid & 63) == 0) atomicMax(&sh.umax, u_out);
+          int64_t t_in, t_all;
+          block_exclusive_scan(u_in, sh.wsum, t_in);
+          __syncthreads();  // the first scan's partial sums are read
+          block_exclusive_scan(u_all, sh.wsum, t_all);
+          const int64_t tau_head = ((int64_t)R << 38) + t_in, tau_all = ((int64_t)R << 38) + t_all;
+          const int64_t um = (int64_t)sh.umax;
+          double mx = 0.0;
+          for (int cnt_c = m + 1 + tid; cnt_c <= n; cnt_c += kThreads) {
+            const int64_t tb = min(tau_head + (int64_t)(cnt_c - m) * um, tau_all);
+            mx = fmax(mx, ldexp((double)tb, -38) * (double)sps[R + cnt_c - 1]);
+          }
+          const unsigned long long mb = wave_max_u64((unsigned long long)__double_as_longlong(mx));
+        if ((tid & 63) == 0) atomicMax(&sh.rest_bits, mb);
+          __syncthreads();
+          rest_bound = __longlong_as_double((long long)sh.rest_bits);
+        }
+        if (finish_schedule<1, MODE>(head_keys, m, true, R, gamma, n, sps, sp1, sps_r, keys, sh,
+                                     lengths, stats, theta_path, k_io, rest_bound))
+          return;
       }
-      if (finish_schedule<1, MODE>(head_keys, m, true, R, gamma, n, sps, sp1, sps_r, keys, sh,
-                                   lengths, stats, theta_path, k_io))
-        return;
     }
   }
   radix_sort<E>(keys, cnt, sh.wsum);

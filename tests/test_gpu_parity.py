@@ -344,8 +344,9 @@ def _head_size(a):
 def test_schedule_head_of_order(dev, R, gamma):
     """Algorithm 1 stopping at chosen places around the end of the head of the
     survival order (an SPS table flat up to B = R + p and tiny after it stops
-    at place p), and top-K counts around it: lengths, statistics and the Theta
-    path equal the oracle's whether or not the stop lies inside the head.
+    at place p, and puts the capacity's largest Theta at count p), and top-K
+    counts around it: lengths, statistics, the Theta path and the capacity
+    equal the oracle's whether or not the place lies inside the head.
     R*gamma > 8192 runs 16 keys per thread."""
     import torch
     from oracle import oracle as O
@@ -367,6 +368,15 @@ def test_schedule_head_of_order(dev, R, gamma):
         np.testing.assert_array_equal(gs["lengths"].cpu().numpy(), os_["lengths"])
         np.testing.assert_array_equal(gs["stats"].cpu().numpy(), os_["stats"])
         np.testing.assert_array_equal(gs["theta_path"].cpu().numpy(), os_["theta_path"])
+        # the capacity without a Theta path: largest Theta at count p, inside
+        # or past the head
+        oc = O.schedule_capacity(a, sps)
+        gc = dev.schedule_capacity(to_dev(c), to_dev(sps), with_path=False)
+        torch.cuda.synchronize()
+        assert int(gc["K"].cpu()[0]) == oc["K"]
+        np.testing.assert_array_equal(gc["stats"].cpu().numpy(), oc["stats"])
+        np.testing.assert_array_equal(gc["lengths"].cpu().numpy(),
+                                      O.schedule_topk(a, sps, oc["K"])["lengths"])
     sps = np.full(R + n, 100.0, np.float32)
     for K in sorted({0, 1, h - 1, h, h + 1, n - 1, n}):
         ot = O.schedule_topk(a, sps, K)

@@ -59,6 +59,14 @@ def test_capacity_and_topk(dev, R, gamma, kind):
         np.testing.assert_array_equal(gc["theta_path"].cpu().numpy(), oc["theta_path"])
         np.testing.assert_array_equal(gc["lengths"].cpu().numpy(),
                                       O.schedule_topk(a, sps, oc["K"])["lengths"])
+        # without the Theta path (above 1024 candidates the head of the
+        # survival order may decide the capacity alone)
+        gn = dev.schedule_capacity(to_dev(c), to_dev(sps), with_path=False)
+        torch.cuda.synchronize()
+        assert int(gn["K"].cpu()[0]) == oc["K"]
+        np.testing.assert_array_equal(gn["a"].cpu().numpy(), a)
+        np.testing.assert_array_equal(gn["stats"].cpu().numpy(), oc["stats"])
+        np.testing.assert_array_equal(gn["lengths"].cpu().numpy(), gc["lengths"].cpu().numpy())
         # the next-but-one round: a new set of confidences verified up to the
         # capacity left on the device (zero-overhead scheduling)
         c2 = _confidences(rng, R, gamma, kind)
