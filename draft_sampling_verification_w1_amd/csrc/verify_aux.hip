@@ -175,6 +175,18 @@ __global__ __launch_bounds__(256) void k_decide(int R, int gamma, int V, uint64_
   const int L = w.req_len[r];
   const int off = w.req_off[r];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  // 0. what the acceptance test needs besides lse_t, fetched first so that the
+  //    token -> T[x] round trip overlaps the merge of the lse partials:
+  //    thread k - 1 holds position k's T[x], log q and ln u (gamma <= 64)
+  double tx = 0.0, lq = 0.0, lnu = 0.0;
+  const int kt = (int)threadIdx.x + 1;
+  if (kt <= L) {
+    const int64_t o = (int64_t)r * gamma + (kt - 1);
+    const int x = min(max(tokens[o], 0), V - 1);
+    tx = (double)elem_at(T, ((int64_t)r * (gamma + 1) + (kt - 1)) * (int64_t)V + x);
+    lq = logq[o];
+    lnu = log(uniform_f64(noise_block(seed, kStreamAccept, r, kt, 0).x));
+  }
   // 1. lse of each verified target row: wave q merges the split partials of
   //    positions q + 1, q + 5, ... (no workgroup barrier per position)
   int chunk;
@@ -199,14 +211,7 @@ __global__ __launch_bounds__(256) void k_decide(int R, int gamma, int V, uint64_
     if (lse_t_out) lse_t_out[(int64_t)r * (gamma + 1) + (k - 1)] = v;
   }
   // 2. every verified position's test at once: accept x_k iff ln u < ln p^t(x_k) - ln p^d(x_k)
-  for (int k = threadIdx.x + 1; k <= L; k += 256) {
-    const int64_t o = (int64_t)r * gamma + (k - 1);
-    const int x = min(max(tokens[o], 0), V - 1);
-    const double tx = (double)elem_at(T, ((int64_t)r * (gamma + 1) + (k - 1)) * (int64_t)V + x);
-    const double rho = (tx - lse_k[k - 1]) - logq[o];
-    const uint32_t wd = noise_block(seed, kStreamAccept, r, k, 0).x;
-    ok_k[k - 1] = log(uniform_f64(wd)) < rho ? 1 : 0;
-  }
+  if (kt <= L) ok_k[kt - 1] = lnu < (tx - lse_k[kt - 1]) - lq ? 1 : 0;
   __syncthreads();
   // 3. the first rejection ends the accepted prefix
   if (threadIdx.x == 0) {
