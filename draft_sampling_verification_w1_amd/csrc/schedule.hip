@@ -151,7 +151,10 @@ __device__ __forceinline__ bool finish_schedule(const uint64_t* ks, int m, bool 
   constexpr bool kEarly = EE <= 8;
   const int tid = threadIdx.x;
   const int base = EE * tid;
-#define SPS_AT(q) (kEarly ? sp[(q)] : sps[R + base + (q) - 1])
+  auto sps_at = [&](int q) -> float {
+    if constexpr (kEarly) return sp[q];
+    else return sps[R + base + q - 1];
+  };
   if (tid == 0) {
     // kTopK: the count handed over (clamped to [0, n]); otherwise "no stop yet"
     int k0 = m;
@@ -180,9 +183,9 @@ __device__ __forceinline__ bool finish_schedule(const uint64_t* ks, int m, bool 
     for (int q = 0; q < EE; ++q) {
       const int i = base + q;
       if (i < m) {
-        const double before = ldexp((double)tau, -38) * (double)SPS_AT(q);
+        const double before = ldexp((double)tau, -38) * (double)sps_at(q);
         tau += tau_unit(e[q]);
-        const double after = ldexp((double)tau, -38) * (double)SPS_AT(q + 1);
+        const double after = ldexp((double)tau, -38) * (double)sps_at(q + 1);
         if (!(after > before) && my_stop == m) my_stop = i;
       }
     }
@@ -198,7 +201,7 @@ __device__ __forceinline__ bool finish_schedule(const uint64_t* ks, int m, bool 
       th[q] = -1.0;
       if (i < m) {
         tau += tau_unit(e[q]);
-        th[q] = ldexp((double)tau, -38) * (double)SPS_AT(q + 1);
+        th[q] = ldexp((double)tau, -38) * (double)sps_at(q + 1);
         mx = fmax(mx, th[q]);
       }
     }
@@ -243,7 +246,7 @@ __device__ __forceinline__ bool finish_schedule(const uint64_t* ks, int m, bool 
     if (i < m) {
       const uint32_t o = (uint32_t)e[q];
       tau += tau_unit(e[q]);
-      const double th = ldexp((double)tau, -38) * (double)SPS_AT(q + 1);
+      const double th = ldexp((double)tau, -38) * (double)sps_at(q + 1);
       if (i < sel) atomicMax(&len[o / gamma], (int)(o % gamma) + 1);
       // Algorithm 1 records the path up to and including the stopping step;
       // the capacity search records all of it
@@ -271,7 +274,6 @@ __device__ __forceinline__ bool finish_schedule(const uint64_t* ks, int m, bool 
   }
   return true;
 }
-#undef SPS_AT
 
 // E candidates per thread (E * 1024 >= R * gamma).  MODE: kAlg1 (causal
 // stop), kCapacity (argmax of Theta over the whole path; K written to
