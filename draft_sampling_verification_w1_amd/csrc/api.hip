@@ -523,9 +523,13 @@ __attribute__((visibility("default"))) int dspark_verify(
   w.ns_b = L.ns_b;
   w.grid_t = L.grid_t;
   w.vec_ok = rows_vec_ok(p, nullptr, T);
+  w.all_rows = lengths == nullptr ? 1 : 0;
 
-  hipError_t e = launch_build_rows(p->R, p->gamma, lengths, w, s);
-  if (e != hipSuccess) return hip_fail(e, "verify rows");
+  hipError_t e = hipSuccess;
+  if (!w.all_rows) {
+    e = launch_build_rows(p->R, p->gamma, lengths, w, s);
+    if (e != hipSuccess) return hip_fail(e, "verify rows");
+  }
   e = launch_target_lse(bf16, p->R, p->gamma, p->V, T, w, s);
   if (e != hipSuccess) return hip_fail(e, "target lse");
   e = launch_decide(bf16, p->R, p->gamma, p->V, p->seed, T, tokens, logq, w, n_accept, accept_mask,

@@ -192,6 +192,8 @@ struct VerifyWs {
   int ns_t, ns_c, ns_r, ns_b;  // ns_t, ns_c: target-lse / c* records per row (their stride)
   int grid_t, grid_c;         // workgroups of the target-lse / c* pass (split counts follow the rows)
   int vec_ok;           // T rows 16-byte aligned: vector loads allowed
+  int all_rows;         // every position verified: the target-lse pass writes the identity
+                        // row map, the per-request bookkeeping and the counts
 };
 
 // Vocabulary splits of the target-lse pass over `active` rows (known on the

@@ -105,14 +105,33 @@ __global__ __launch_bounds__(1024) void k_build_rows(int R, int gamma, const int
 template <typename E>
 __global__ __launch_bounds__(256) void k_target_lse(int gamma, int V, const E* T, VerifyWs w) {
   const int nrows = (int)gridDim.x;  // every position
-  const int active = min(w.counts[0], nrows);
+  const bool all = w.all_rows != 0;
+  if (all && blockIdx.y == 0 && threadIdx.x == 0) {
+    // every position verified: the row map is the identity, written here in
+    // place of a row-building pass (later kernels read it; this one does not)
+    const int x = (int)blockIdx.x;
+    w.row_ids[x] = x;
+    if (x < nrows / gamma) {
+      w.req_off[x] = x * gamma;
+      w.req_len[x] = gamma;
+      w.req_mode[x] = 0;
+      w.req_slot[x] = 0;
+    }
+    if (x == 0) {
+      w.counts[0] = nrows;
+      w.counts[1] = 0;
+      w.counts[2] = 0;
+      w.counts[3] = 0;
+    }
+  }
+  const int active = all ? nrows : min(w.counts[0], nrows);
   int chunk;
   const int ns = lse_split_count(active, w.grid_t, V, &chunk);
   const int wg = (int)(blockIdx.x + gridDim.x * blockIdx.y);
   const int i = wg / ns;
   if (i >= active) return;
   const int split = wg - i * ns;
-  const int id = w.row_ids[i];
+  const int id = all ? i : w.row_ids[i];
   const int r = id / gamma;
   const int k = id - r * gamma + 1;
   const E* row = T + ((int64_t)r * (gamma + 1) + (k - 1)) * (int64_t)V;
