@@ -129,10 +129,8 @@ KERNELS = {
     "target_lse": ("k_target_lse<unsigned short>", "csrc/verify_aux.hip"),
     "decide": ("k_decide<unsigned short>", "csrc/verify_aux.hip"),
     "bonus": ("k_bonus<unsigned short>", "csrc/verify_aux.hip"),
-    "finalize": ("k_finalize", "csrc/verify_aux.hip"),
     "draft_select": ("k_select<0>", "csrc/select.hip"),
-    "residual_select": ("k_select<1>", "csrc/select.hip"),
-    "bonus_select": ("k_select<2>", "csrc/select.hip"),
+    "final_select": ("k_select_final", "csrc/select.hip"),
     "schedule": ("k_schedule<4, 0>", "csrc/schedule.hip"),
 }
 

@@ -577,7 +577,7 @@ __attribute__((visibility("default"))) int dspark_verify(
   e = launch_bias_pass(kModeResidual, bf16, a, s);
   if (e != hipSuccess) return hip_fail(e, "residual pass");
   // ... and the bonus draw's block records
-  e = launch_bonus(bf16, p->R, p->gamma, p->V, p->seed, T, w, s);
+  e = launch_bonus(bf16, p->R, p->gamma, p->V, p->seed, T, w, cstar, s);  // also finalizes c*
   if (e != hipSuccess) return hip_fail(e, "bonus pass");
   SelectArgs q = {};
   q.R = p->R;
@@ -601,17 +601,14 @@ __attribute__((visibility("default"))) int dspark_verify(
   q.cand = w.r_cand;
   q.cand_f = w.r_candf;
   q.wpos = w.r_wpos;
-  e = launch_select(kSelResidual, bf16, q, s);
-  if (e != hipSuccess) return hip_fail(e, "residual select");
-  q.row_ids = w.bonus_ids;
-  q.row_count = w.counts + 2;
-  q.nsplit = L.ns_b;
-  q.tiles_per_stage = 1;
-  q.cand = w.b_cand;
-  e = launch_select(kSelBonus, bf16, q, s);
-  if (e != hipSuccess) return hip_fail(e, "bonus select");
-  e = launch_finalize(p->R, p->gamma, w, cstar, s);
-  if (e != hipSuccess) return hip_fail(e, "finalize");
+  SelectArgs qb = q;
+  qb.row_ids = w.bonus_ids;
+  qb.row_count = w.counts + 2;
+  qb.nsplit = L.ns_b;
+  qb.tiles_per_stage = 1;
+  qb.cand = w.b_cand;
+  e = launch_select_final(bf16, q, qb, s);
+  if (e != hipSuccess) return hip_fail(e, "residual / bonus select");
   return ok();
 }
 

@@ -169,6 +169,10 @@ struct SelectArgs {
   double* out_logq;           // draft
 };
 hipError_t launch_select(int mode, bool bf16, const SelectArgs& a, hipStream_t stream);
+// Residual and bonus draws of a verify in one launch (a: residual list, b: bonus list;
+// the two lists hold every request once).
+hipError_t launch_select_final(bool bf16, const SelectArgs& ar, const SelectArgs& ab,
+                               hipStream_t stream);
 
 
 // ---- verification helpers ------------------------------------------------
@@ -222,8 +226,7 @@ hipError_t launch_decide(bool bf16, int R, int gamma, int V, uint64_t seed, cons
                          int32_t* n_accept, uint8_t* accept_mask, double* lse_t_out,
                          hipStream_t stream);
 hipError_t launch_bonus(bool bf16, int R, int gamma, int V, uint64_t seed, const void* T,
-                        const VerifyWs& w, hipStream_t stream);
-hipError_t launch_finalize(int R, int gamma, const VerifyWs& w, float* cstar, hipStream_t stream);
+                        const VerifyWs& w, float* cstar, hipStream_t stream);
 
 // ---- other stages ---------------------------------------------------------
 hipError_t launch_pack_w2(bool bf16, int V, const void* W2, void* W2p, hipStream_t stream);

@@ -28,6 +28,18 @@ __global__ __launch_bounds__(256) void k_select(const SelectArgs a, int bf16_fla
   sel::select_row<MODE>(a, bf16_flag, blockIdx.x, sh, a.k);
 }
 
+// The verify's final draws in one launch, one workgroup per request: every
+// request is on exactly one of the two lists (a rejection, or full acceptance
+// and a bonus draw), the residual list first.
+__global__ __launch_bounds__(256) void k_select_final(const SelectArgs ar, const SelectArgs ab,
+                                                      int bf16_flag) {
+  __shared__ sel::SelShared sh;
+  const int nres = *ar.row_count;
+  const int i = (int)blockIdx.x;
+  if (i < nres) sel::select_row<kSelResidual>(ar, bf16_flag, i, sh, 0);
+  else sel::select_row<kSelBonus>(ab, bf16_flag, i - nres, sh, 0);
+}
+
 }  // namespace
 
 hipError_t launch_select(int mode, bool bf16, const SelectArgs& a, hipStream_t stream) {
@@ -45,6 +57,16 @@ hipError_t launch_select(int mode, bool bf16, const SelectArgs& a, hipStream_t s
     TimingScope timing("bonus_select", stream);
     hipLaunchKernelGGL(k_select<kSelBonus>, dim3(a.R), dim3(256), 0, stream, a, flag);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_select_final(bool bf16, const SelectArgs& ar, const SelectArgs& ab,
+                               hipStream_t stream) {
+  if (ar.nsplit < 1 || ar.nsplit > 256 * sel::RecSlots<kSelResidual>::K) return hipErrorInvalidValue;
+  if (ab.nsplit < 1 || ab.nsplit > 256 * sel::RecSlots<kSelBonus>::K) return hipErrorInvalidValue;
+  if (ar.R != ab.R) return hipErrorInvalidValue;
+  TimingScope timing("final_select", stream);
+  hipLaunchKernelGGL(k_select_final, dim3(ar.R), dim3(256), 0, stream, ar, ab, bf16 ? 1 : 0);
   return hipGetLastError();
 }
 

@@ -1,12 +1,14 @@
 // verify_aux.hip -- the verification steps that need no Markov-head bias:
-//   build_rows : (request, position) rows to verify, k <= l_r
+//   build_rows : (request, position) rows to verify, k <= l_r (with per-request
+//                lengths; when every position is verified the target pass
+//                writes the identity row map)
 //   target_lse : log-sum-exp of every verified target row (split vocabulary)
 //   decide     : acceptance test of each drafted token, first rejection,
 //                residual / bonus work lists (standard speculative rejection
 //                sampling; notes page 배경, summary page 요약)
 //   bonus      : first level of the two-level Gumbel-max draw over T[r, l_r]
-//                when every verified token is accepted (bonus token from p^t_{l_r+1})
-//   finalize   : c* per (request, position)
+//                when every verified token is accepted (bonus token from p^t_{l_r+1});
+//                its first split's workgroups also sum c* per (request, position)
 #include "device_common.h"
 #include "kernels.h"
 
@@ -261,16 +263,43 @@ __global__ __launch_bounds__(256) void k_decide(int R, int gamma, int V, uint64_
   }
 }
 
+// c* of request r's positions, one wave per position: the sum of the
+// position's vocabulary splits (NaN beyond the request's verify length).  Run
+// by the bonus pass, which follows the c* pass on the stream.
+__device__ __forceinline__ void finalize_request(int r, int R, int gamma, const VerifyWs& w,
+                                                 float* cstar) {
+  const int lane = threadIdx.x & 63;
+  // the c* pass's split count for this many verified rows (records at stride ns_c)
+  const int ns = active_split_count(w.grid_c, min(w.counts[0], R * gamma), w.ns_c);
+  const int L = w.req_len[r];
+  for (int k = (int)(threadIdx.x >> 6) + 1; k <= gamma; k += 4) {
+    const int64_t item = (int64_t)r * gamma + (k - 1);
+    if (k > L) {
+      if (lane == 0) cstar[item] = NAN;
+      continue;
+    }
+    const int64_t base = (int64_t)(w.req_off[r] + k - 1) * w.ns_c;
+    double s = 0.0;
+    for (int j = lane; j < ns; j += 64) s += w.c_s[base + j];
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) s += __shfl_xor(s, off, 64);
+    if (lane == 0) cstar[item] = (float)s;
+  }
+}
+
 // Bonus draw, first level: per 32-token block of the target row T[r, l_r]
 // (p^t_{l_r+1}), the block log-mass plus its Gumbel variate (stream 3), kept
 // as split records for the binary64 select stage.  A quad of threads covers
 // one block (8 tokens each).
+// The workgroups of the first split also finalize c* of request blockIdx.x
+// (the grid has one column per request).
 template <typename E>
 __global__ __launch_bounds__(256) void k_bonus(int gamma, int V, uint64_t seed, const E* T,
-                                               VerifyWs w) {
+                                               VerifyWs w, float* cstar) {
   __shared__ float slo[4], shi1[4], shi2[4];
   __shared__ int sb1[4];
   const int i = blockIdx.x;
+  if (blockIdx.y == 0) finalize_request(i, (int)gridDim.x, gamma, w, cstar);
   if (i >= w.counts[2]) return;
   const int id = w.bonus_ids[i];
   const int r = id / (gamma + 1);
@@ -357,28 +386,6 @@ __global__ __launch_bounds__(256) void k_bonus(int gamma, int V, uint64_t seed, 
   }
 }
 
-// One wave per (request, position) entry: c* = sum of its vocabulary splits
-// (NaN beyond the request's verify length).
-__global__ __launch_bounds__(256) void k_finalize(int R, int gamma, VerifyWs w, float* cstar) {
-  const int lane = threadIdx.x & 63;
-  const int item = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (item >= R * gamma) return;
-  const int r = item / gamma;
-  const int k = item - r * gamma + 1;
-  if (k > w.req_len[r]) {
-    if (lane == 0) cstar[item] = NAN;
-    return;
-  }
-  // the c* pass's split count for this many verified rows (records at stride ns_c)
-  const int ns = active_split_count(w.grid_c, min(w.counts[0], R * gamma), w.ns_c);
-  const int64_t base = (int64_t)(w.req_off[r] + k - 1) * w.ns_c;
-  double s = 0.0;
-  for (int j = lane; j < ns; j += 64) s += w.c_s[base + j];
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) s += __shfl_xor(s, off, 64);
-  if (lane == 0) cstar[item] = (float)s;
-}
-
 }  // namespace
 
 hipError_t launch_build_rows(int R, int gamma, const int32_t* lengths, const VerifyWs& w,
@@ -415,21 +422,15 @@ hipError_t launch_decide(bool bf16, int R, int gamma, int V, uint64_t seed, cons
 }
 
 hipError_t launch_bonus(bool bf16, int R, int gamma, int V, uint64_t seed, const void* T,
-                        const VerifyWs& w, hipStream_t stream) {
+                        const VerifyWs& w, float* cstar, hipStream_t stream) {
   TimingScope timing("bonus", stream);
   const dim3 grid(R, w.ns_b);
   if (bf16)
     hipLaunchKernelGGL(k_bonus<uint16_t>, grid, dim3(256), 0, stream, gamma, V, seed,
-                       (const uint16_t*)T, w);
+                       (const uint16_t*)T, w, cstar);
   else
-    hipLaunchKernelGGL(k_bonus<float>, grid, dim3(256), 0, stream, gamma, V, seed, (const float*)T, w);
-  return hipGetLastError();
-}
-
-hipError_t launch_finalize(int R, int gamma, const VerifyWs& w, float* cstar, hipStream_t stream) {
-  TimingScope timing("finalize", stream);
-  const int waves = R * gamma;
-  hipLaunchKernelGGL(k_finalize, dim3((waves + 3) / 4), dim3(256), 0, stream, R, gamma, w, cstar);
+    hipLaunchKernelGGL(k_bonus<float>, grid, dim3(256), 0, stream, gamma, V, seed, (const float*)T, w,
+                       cstar);
   return hipGetLastError();
 }
 
