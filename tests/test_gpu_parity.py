@@ -226,15 +226,15 @@ def test_draft_is_deterministic(dev):
     assert not torch.equal(r1[0], r3)
 
 
-@pytest.mark.parametrize("R,gamma,V,dtype", [(48, 3, 6000, "qwen3_4b"), (300, 4, 3000, "high_concurrency"),
-                                              (5, 6, 1001, "tiny")])
-def test_verify_all_positions_two_ways(dev, R, gamma, V, dtype):
+@pytest.mark.parametrize("R,gamma,V,workload", [(48, 3, 6000, "qwen3_4b"), (300, 4, 3000, "high_concurrency"),
+                                                 (5, 6, 1001, "tiny")])
+def test_verify_all_positions_two_ways(dev, R, gamma, V, workload):
     """Verifying every position without per-request lengths (the target pass
     writes the identity row map) and with every length set to gamma (a row
     pass builds the map) give the same c*, acceptances, draws and lse_t."""
     import torch
     from draft_sampling_verification_w1_amd import synth
-    cfg = synth.scaled(synth.CONFIGS[dtype], name=f"all_{R}", R=R, gamma=gamma, V=V,
+    cfg = synth.scaled(synth.CONFIGS[workload], name=f"all_{R}", R=R, gamma=gamma, V=V,
                        n_sps=R * (gamma + 1))
     inp = gen_inputs(cfg)
     U, W1, A = to_dev(inp["U"]), to_dev(inp["W1"]), to_dev(inp["anchors"])
